@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+One step is one fa_fwd call (the whole forward hot path: schedule, Q load,
+K/V streaming, QK^T, masking, online softmax, PV, epilogue) over the
+workload's batch, with inputs already resident in HBM. Prints one JSON line
+with the throughput in TFLOP/s (4*B*H*N_q*N_kv*d, halved when causal), the
+roofline fraction against the dense-bf16 MFMA peak, and the CPU oracle timed
+on a bounded sample of the same workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS, make_inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_fa_fwd.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the forward kernel is built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_109_amd", "csrc")
+    for f in ("fa_device.hpp", "fa_fwd_bf16.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if rec.get("kernel_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    G = w.H_q // w.H_kv
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H_q):
+            oracle.head_forward(q[b, h], k[b, h // G], v[b, h // G], w.causal, w.scale)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flop = w.fwd_flop / (w.B * w.H_q) * heads
+    return {
+        "value": flop / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H_q} heads (all {w.N_q} rows each) of {w.name}, fp64 numpy, "
+                  f"{el:.1f} s",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path is "
+              "single-GPU; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_109_amd as fa
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+
+    w = WORKLOADS[args.workload]
+    print(f"# workload {w}", file=sys.stderr, flush=True)
+    inp = make_inputs(w)
+    q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
+
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        per[i][0].record(stream)
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        per[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    launch_ms = [a.elapsed_time(b) for a, b in per]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(np.mean(launch_ms))
+    tflops = w.fwd_flop / (ms_per_step * 1e-3) / 1e12
+    achieved = w.fwd_flop / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == 1 else PEAK_F32_TFLOPS
+
+    props = torch.cuda.get_device_properties(0)
+    result = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) and fraction of MI355X dense-bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == 1 else "f32",
+        "data": "synthetic: i.i.d. N(0,1) from PCG64(seed), rounded to bf16",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N_q": w.N_q, "N_kv": w.N_kv,
+                   "d": w.d, "causal": w.causal, "scale": w.scale, "seed": w.seed},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": "fwd_bf16_kernel" if w.dtype == 1 else "fwd_f32_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "flop_per_launch": w.fwd_flop,
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

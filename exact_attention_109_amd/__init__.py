@@ -1,0 +1,172 @@
+"""Exact attention on AMD MI355X (gfx950): Python binding of libfa.so.
+
+The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
+fa_bwd_workspace_size and fa_status_string. This module exposes the same
+four names with the same arguments (device pointers as integers, sizes,
+flags, a stream handle) plus two convenience wrappers over torch tensors:
+
+    o, lse = fwd(q, k, v, causal=False, scale=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
+
+The wrappers only marshal arguments: torch allocates device memory and
+supplies the current stream; every step of the computation runs in the HIP
+kernels of libfa.so. There is no fallback path: if the library is missing
+or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                           " or `python exact_attention_109_amd/_build.py`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# The C entry points, one to one
+# ---------------------------------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, stream) -> int:
+    return load_library().fa_fwd(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, int(causal), float(scale),
+                                 dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H_q, H_kv, N_q, N_kv, d,
+           causal, scale, dtype, stream) -> int:
+    return load_library().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H_q, H_kv,
+                                 N_q, N_kv, d, int(causal), float(scale), dtype, stream)
+
+
+def fa_bwd_workspace_size(B, H_q, N_q) -> int:
+    return load_library().fa_bwd_workspace_size(B, H_q, N_q)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch tensor wrappers
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream_handle(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Attention forward on tensors q [B,H_q,N_q,d], k and v [B,H_kv,N_kv,d].
+
+    Returns (o, lse): o like q, lse float32 [B,H_q,N_q] (natural log)."""
+    import torch
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    _check(q, "q")
+    _check(k, "k", q.dtype, (B, H_kv, N_kv, d))
+    _check(v, "v", q.dtype, (B, H_kv, N_kv, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    _check(out, "out", q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H_q, H_kv, N_q, N_kv, d, causal, scale, _dtype_code(q), _stream_handle(q))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
+    """Attention backward; o and lse from fwd on the same inputs.
+
+    Returns (dq, dk, dv), all float32."""
+    import torch
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    _check(q, "q")
+    _check(k, "k", q.dtype, (B, H_kv, N_kv, d))
+    _check(v, "v", q.dtype, (B, H_kv, N_kv, d))
+    _check(o, "o", q.dtype, q.shape)
+    _check(do, "do", q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    ws_bytes = fa_bwd_workspace_size(B, H_q, N_q)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                B, H_q, H_kv, N_q, N_kv, d, causal, scale, _dtype_code(q), _stream_handle(q))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fwd", "bwd", "load_library",
+           "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
+           "FA_DTYPE_BF16", "LIB_PATH"]

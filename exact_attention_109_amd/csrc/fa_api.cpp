@@ -1,0 +1,165 @@
+// C-ABI front end of libfa.so: argument validation (pure C++, no HIP call),
+// device check, kernel selection and launch. The operation and the argument
+// conventions are documented in include/fa.h.
+
+#include "fa.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "fa_internal.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxSeq = int64_t(1) << 24;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
+
+// Shared shape checks. Returns FA_OK and sets *empty when there is nothing to do.
+int check_shape(int B, int H_q, int H_kv, int N_q, int N_kv, int d, float scale, int dtype,
+                bool* empty) {
+  *empty = false;
+  if (B < 0 || H_q < 0 || H_kv < 0 || N_q < 0 || N_kv < 0 || d < 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H_q == 0 || N_q == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (H_kv == 0 || H_q % H_kv != 0) return FA_ERR_INVALID_ARG;
+  if (N_kv == 0) return FA_ERR_INVALID_ARG;
+  if (N_q > kMaxSeq || N_kv > kMaxSeq) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Device check: gfx950 only. Cached per device id (0 = unknown, 1 = ok, 2 = not ok).
+std::atomic<int> g_device_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return FA_ERR_UNSUPPORTED;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+FA_EXPORT const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid pointer, size, scale or workspace argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported dtype, head dimension, scale sign or device";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown fa status code";
+  }
+}
+
+FA_EXPORT int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                     int causal, float scale, int dtype, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+
+  const size_t es = elem_size(dtype);
+  const size_t q_bytes = size_t(B) * H_q * N_q * d * es;
+  const size_t kv_bytes = size_t(B) * H_kv * N_kv * d * es;
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  const Range in[3] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(v, kv_bytes)};
+  const Range out[2] = {range_of(o, q_bytes), range_of(lse, lse_bytes)};
+  for (const Range& r : out)
+    for (const Range& i : in)
+      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::FwdParams p{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, s) : fa::launch_fwd_f32(p, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_EXPORT size_t fa_bwd_workspace_size(int B, int H_q, int N_q) {
+  if (B <= 0 || H_q <= 0 || N_q <= 0) return 0;
+  size_t bytes = size_t(B) * H_q * N_q * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                     int causal, float scale, int dtype, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) {
+    // No query rows: dk and dv would be all zero, but with B or H_q zero there
+    // is nothing to write; with N_q zero and keys present the caller gets FA_OK
+    // and no writes, as documented for empty problems.
+    return FA_OK;
+  }
+
+  const size_t es = elem_size(dtype);
+  const size_t q_bytes = size_t(B) * H_q * N_q * d * es;
+  const size_t kv_bytes = size_t(B) * H_kv * N_kv * d * es;
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  const size_t dq_bytes = size_t(B) * H_q * N_q * d * sizeof(float);
+  const size_t dkv_bytes = size_t(B) * H_kv * N_kv * d * sizeof(float);
+  const size_t ws_need = fa_bwd_workspace_size(B, H_q, N_q);
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  const void* ptrs[10] = {q, k, v, o, lse, dO, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  const Range in[6] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(v, kv_bytes),
+                       range_of(o, q_bytes), range_of(lse, lse_bytes), range_of(dO, q_bytes)};
+  const Range out[4] = {range_of(dq, dq_bytes), range_of(dk, dkv_bytes), range_of(dv, dkv_bytes),
+                        range_of(workspace, ws_need)};
+  for (int a = 0; a < 4; ++a) {
+    for (const Range& i : in)
+      if (overlaps(out[a], i)) return FA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(out[a], out[b])) return FA_ERR_INVALID_ARG;
+  }
+  if (workspace_bytes < ws_need) return FA_ERR_INVALID_ARG;
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::BwdParams p{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace),
+                  B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, s) : fa::launch_bwd_f32(p, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI front end (fa_api.cpp) and the kernel
+// translation units. Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // workspace: D_i = <dO_i, o_i>, [B][H_q][N_q] float32
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+};
+
+// Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
+// The front end has already validated every argument.
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fa

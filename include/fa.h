@@ -1,0 +1,129 @@
+/*
+ * fa.h -- C ABI of the exact-attention library (libfa.so) for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * and its gradients, without ever writing the N_q x N_kv score or probability
+ * matrix to device memory.
+ *
+ * Sources for the operation (the pages this library is built from):
+ *   - "FlashAttention" (LLM Inference Handbook, Kernel Optimization), section
+ *     on why attention is slow: the definition softmax(Q K^T / sqrt(d_k)) V;
+ *     section on how FlashAttention works: tiles of Q, K, V are moved on chip,
+ *     the work is fused into one kernel and the N x N matrix is never stored.
+ *   - "深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力" (rkmt.cn blog),
+ *     §2.1 (safe and online softmax) and §2.2 (a Q block stays resident while
+ *     every K/V block streams past it; each row keeps a running max, a
+ *     normalizer and an output accumulator that are rescaled when the max grows).
+ *   - "Flash-Attention" (Awesome System Papers Wiki), core-idea section: the
+ *     backward pass recomputes the probabilities from Q, K, V and a few saved
+ *     per-row statistics; design-space section: causal, non-causal and GQA.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers on the calling thread's current HIP device.
+ *    The caller owns every buffer; the library never allocates, frees or keeps
+ *    a pointer after returning. Every pointer must be 16-byte aligned.
+ *  - All tensors are contiguous row-major:
+ *        q, o, dO, dq : [B][H_q][N_q][d]
+ *        k, v, dk, dv : [B][H_kv][N_kv][d]
+ *        lse          : [B][H_q][N_q]            (float32)
+ *  - dtype: FA_DTYPE_F32 (float32) or FA_DTYPE_BF16 (bfloat16). It applies to
+ *    q, k, v, o and dO. lse, dq, dk and dv are always float32.
+ *  - GQA: H_q must be a multiple of H_kv; query head h reads key/value head
+ *    h / (H_q / H_kv) (integer division: consecutive query heads share).
+ *  - causal != 0: query row i may attend key j only when j <= i (aligned at the
+ *    top-left corner for every N_q, N_kv). causal == 0: every key is allowed.
+ *  - scale multiplies Q K^T; it must be finite and >= 0. The usual value is
+ *    1/sqrt(d).
+ *  - Supported head dimensions: d = 64 or d = 128. N_q, N_kv <= 2^24.
+ *  - stream: a hipStream_t (NULL = the default stream). Calls are asynchronous
+ *    with respect to the host; faults inside a kernel surface at the caller's
+ *    next synchronization.
+ *  - Argument checks happen before any HIP call, in this order: negative
+ *    sizes; dtype; d; empty problem (B, H_q or N_q zero -> FA_OK, nothing
+ *    launched); H_kv; N_kv; sizes; scale; null and misaligned pointers;
+ *    overlap of an output with an input or another output; workspace. Then
+ *    the device is checked (gfx950) and the kernels are launched.
+ *  - Results are deterministic: the same inputs give bitwise equal outputs.
+ *  - No global mutable state besides a per-device cache of the device check;
+ *    concurrent calls on different streams are safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define FA_OK 0              /* success (work enqueued on the stream) */
+#define FA_ERR_INVALID_ARG 1 /* a pointer, size, scale or workspace argument is invalid */
+#define FA_ERR_UNSUPPORTED 2 /* dtype, head dimension, negative scale or device not supported */
+#define FA_ERR_HIP 3         /* the HIP runtime reported an error at launch */
+
+/* Element types for q, k, v, o, dO. */
+#define FA_DTYPE_F32 0
+#define FA_DTYPE_BF16 1
+
+/*
+ * fa_fwd -- attention forward.
+ *
+ * For every batch b, query head h and query row i (h_kv = h / (H_q/H_kv)):
+ *     s_ij      = scale * <q[b,h,i,:], k[b,h_kv,j,:]>      over the allowed keys j
+ *     lse[b,h,i]= ln sum_j exp(s_ij)                         (natural log, float32)
+ *     o[b,h,i,:]= sum_j exp(s_ij - lse[b,h,i]) * v[b,h_kv,j,:]
+ * This is the attention definition of the Handbook page with the safe-softmax
+ * of blog §2.1, evaluated by the blockwise update of blog §2.2.
+ *
+ * Inputs : q, k, v (dtype). Outputs: o (dtype; bf16 results are rounded to
+ * nearest even) and lse (float32); every element of both is written.
+ * Errors : see the conventions above. N_kv = 0 with a non-empty problem is
+ * FA_ERR_INVALID_ARG (softmax over no keys is undefined).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+           int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for a
+ * problem with B batches, H_q query heads and N_q query rows (a multiple of
+ * 256). The workspace holds per-row float32 statistics; its content on entry
+ * does not matter and on return is unspecified.
+ */
+size_t fa_bwd_workspace_size(int B, int H_q, int N_q);
+
+/*
+ * fa_bwd -- attention backward by recomputation (Wiki core-idea section: the
+ * probabilities are rebuilt from q, k, v and the saved lse instead of being
+ * stored by the forward pass).
+ *
+ * Gradients of the scalar L = sum(dO * o), with P_ij = exp(s_ij - lse_i):
+ *     dv_j = sum_i P_ij dO_i
+ *     dS_ij= P_ij * (<dO_i, v_j> - D_i),   D_i = <dO_i, o_i>
+ *     dq_i = scale * sum_j dS_ij k_j
+ *     dk_j = scale * sum_i dS_ij q_i
+ * where o and lse are the outputs of fa_fwd on the same q, k, v. For GQA the
+ * dk and dv of a key/value head sum over its H_q/H_kv query heads.
+ *
+ * Inputs : q, k, v, o, dO (dtype), lse (float32).
+ * Outputs: dq, dk, dv (float32), fully written; keys no query may attend get 0.
+ * workspace: device memory of at least fa_bwd_workspace_size(B, H_q, N_q)
+ * bytes, 16-byte aligned, not overlapping any other argument.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, float* dq, float* dk, float* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+           int causal, float scale, int dtype, void* stream);
+
+/* fa_status_string -- a static, NUL-terminated description of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

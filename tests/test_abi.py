@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fa.h declares, and rejects invalid arguments with the documented
+status before making any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.gpu_util import ROOT, ensure_library
+import exact_attention_109_amd as fa
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    ensure_library()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # nothing else with C linkage leaks out under the fa_ prefix
+    assert exported == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        s = fa.fa_status_string(code)
+        assert s.startswith("FA_")
+    assert "unknown" in fa.fa_status_string(12345)
+
+
+def test_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 16, 4096) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3) == 256
+    assert fa.fa_bwd_workspace_size(0, 1, 3) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 65) % 256 == 0
+
+
+# Fake, never dereferenced "device" addresses: validation fails before any use.
+A = 0x10000000
+STEP = 0x01000000
+
+
+def ptrs(n, base=A):
+    return [base + i * STEP for i in range(n)]
+
+
+def fwd_call(**kw):
+    q, k, v, o, lse = ptrs(5)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, B=1, H_q=2, H_kv=1, N_q=16, N_kv=16, d=64, causal=0,
+                scale=0.125, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+def bwd_call(**kw):
+    q, k, v, o, lse, do, dq, dk, dv, ws = ptrs(10)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, dO=do, dq=dq, dk=dk, dv=dv, workspace=ws, workspace_bytes=1 << 20,
+                B=1, H_q=2, H_kv=1, N_q=16, N_kv=16, d=64, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16,
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+INVALID = fa.FA_ERR_INVALID_ARG
+UNSUP = fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("call", [fwd_call, bwd_call])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(N_q=-3), INVALID),
+    (dict(d=-64), INVALID),
+    (dict(dtype=7), UNSUP),
+    (dict(d=96), UNSUP),
+    (dict(d=256), UNSUP),
+    (dict(H_kv=3, H_q=4), INVALID),
+    (dict(H_kv=0), INVALID),
+    (dict(N_kv=0), INVALID),
+    (dict(N_q=(1 << 24) + 1), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(scale=-0.5), UNSUP),
+    (dict(q=0), INVALID),
+    (dict(k=0), INVALID),
+    (dict(lse=0), INVALID),
+    (dict(v=A + 8), INVALID),            # not 16-byte aligned
+    (dict(lse=A + 4), INVALID),          # misaligned and overlapping
+])
+def test_invalid_arguments(call, kw, expect):
+    assert call(**kw) == expect
+
+
+def test_empty_problem_is_a_noop():
+    # Nothing is launched (and no HIP call is made) when there are no rows.
+    assert fwd_call(B=0) == fa.FA_OK
+    assert fwd_call(N_q=0) == fa.FA_OK
+    assert fwd_call(H_q=0, H_kv=0) == fa.FA_OK
+    assert bwd_call(N_q=0) == fa.FA_OK
+    assert fwd_call(N_q=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK
+
+
+def test_output_aliasing_an_input_is_rejected():
+    q, k, v, o, lse = ptrs(5)
+    assert fwd_call(o=q) == INVALID                 # o == q
+    assert fwd_call(o=k + 256) == INVALID           # o starts inside k
+    assert fwd_call(lse=v + 512) == INVALID         # lse inside v
+    assert fwd_call(lse=o + 16) == INVALID          # two outputs overlapping
+    # bwd: gradients and workspace may not overlap inputs or each other
+    base = ptrs(10)
+    assert bwd_call(dq=base[0]) == INVALID
+    assert bwd_call(dk=base[6]) == INVALID
+    assert bwd_call(workspace=base[8]) == INVALID
+    assert bwd_call(dv=base[5] + 32) == INVALID
+
+
+def test_workspace_too_small_is_rejected():
+    assert bwd_call(workspace_bytes=0) == INVALID
+    need = fa.fa_bwd_workspace_size(1, 2, 16)
+    assert bwd_call(workspace_bytes=need - 1) == INVALID

@@ -1,0 +1,198 @@
+"""Forward parity on the GPU: libfa.so through its C ABI against the fp64
+CPU oracle on identical (bf16-rounded) inputs."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import (TOL, bf16_half_ulp, default_scale, ensure_library, max_abs, o_within, sample_rows,
+                            to_f64, upload)
+from workloads import DTYPE_BF16, DTYPE_F32, WORKLOADS, make_inputs, make_inputs_shape
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_library()
+
+
+def run_fwd(inp, causal, scale):
+    import exact_attention_109_amd as fa
+    import torch
+    q, k, v = upload(inp)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+# Shapes: (N_q, N_kv) pairs spanning one and several tiles with ragged tails,
+# crossed with head groupings (H_q, H_kv) for G = 1, 2, 4.
+PAIRS = [(1, 1), (3, 17), (17, 3), (64, 64), (65, 65), (127, 129), (128, 128), (129, 255), (255, 300),
+         (300, 255), (1, 300), (300, 1), (256, 64), (513, 511)]
+HEADS = [(1, 1, 1), (2, 2, 1), (1, 4, 2), (1, 4, 1)]
+
+
+@pytest.mark.parametrize("dtype", [DTYPE_BF16, DTYPE_F32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_shapes_against_oracle(dtype, d, causal):
+    tol = TOL[dtype]
+    seed = 100
+    worst_o = worst_l = 0.0
+    for (nq, nkv) in PAIRS:
+        for (B, Hq, Hkv) in HEADS:
+            seed += 1
+            print(f"case dtype={dtype} d={d} causal={causal} B={B} Hq={Hq} Hkv={Hkv} nq={nq} nkv={nkv}", flush=True)
+            inp = make_inputs_shape(dtype, B, Hq, Hkv, nq, nkv, d, seed)
+            scale = default_scale(d)
+            o, lse = run_fwd(inp, causal, scale)
+            O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), causal, scale)
+            eo, el = max_abs(o, O), max_abs(lse, L)
+            assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+            assert o_within(o, O, dtype), (nq, nkv, B, Hq, Hkv, eo)
+            assert el <= tol["lse"], (nq, nkv, B, Hq, Hkv, el)
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    print(f"worst max-abs O {worst_o:.3e} LSE {worst_l:.3e}")
+
+
+@pytest.mark.parametrize("dtype", [DTYPE_BF16, DTYPE_F32])
+def test_worked_example_through_the_kernel(dtype):
+    """x = [2, 1, 3] from the online-softmax example: one query e_0, keys
+    x_j e_0, values e_j, scale 1 -> O[0:3] = softmax(x), LSE = ln(e^2+e+e^3)."""
+    import torch
+    import exact_attention_109_amd as fa
+    tdt = torch.bfloat16 if dtype == DTYPE_BF16 else torch.float32
+    for d in (64, 128):
+        q = torch.zeros((1, 1, 1, d), dtype=tdt)
+        q[0, 0, 0, 0] = 1
+        k = torch.zeros((1, 1, 3, d), dtype=tdt)
+        k[0, 0, :, 0] = torch.tensor([2.0, 1.0, 3.0])
+        v = torch.zeros((1, 1, 3, d), dtype=tdt)
+        for j in range(3):
+            v[0, 0, j, j] = 1
+        for causal in (False,):
+            o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=1.0)
+            torch.cuda.synchronize()
+            o = to_f64(o)[0, 0, 0]
+            y = np.exp([2.0, 1.0, 3.0]) / np.sum(np.exp([2.0, 1.0, 3.0]))
+            assert o_within(o[:3], y, dtype)
+            assert np.all(o[3:] == 0)
+            assert abs(float(lse.cpu()[0, 0, 0]) - 3.4076059644) <= TOL[dtype]["lse"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_uniform(causal):
+    import torch
+    import exact_attention_109_amd as fa
+    inp = make_inputs_shape(DTYPE_BF16, 1, 2, 1, 200, 200, 64, seed=7)
+    q, k, v = upload(inp)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=0.0)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    V = inp.f64("v")[0, 0]
+    for i in (0, 1, 63, 64, 199):
+        n = (i + 1) if causal else 200
+        assert max_abs(o[0, 1, i], V[:n].mean(axis=0)) <= 1e-2
+        assert abs(lse[0, 1, i] - math.log(n)) <= 1e-3
+
+
+def _row_sample_check(w, inp, o, lse, rng, heads, tol_o, tol_l):
+    """Compare sampled rows of the given (b, h) heads with the oracle
+    (bf16 O: 1e-2 beyond half a bf16 ulp of the exact value, per element)."""
+    G = w.H_q // w.H_kv
+    q = inp.f64("q")
+    k = inp.f64("k")
+    v = inp.f64("v")
+    rows = sample_rows(w.N_q, rng)
+    report = []
+    for (b, h) in heads:
+        hk = h // G
+        O, L = oracle.head_forward(q[b, h], k[b, hk], v[b, hk], w.causal, w.scale, rows)
+        got_o, got_l = o[b, h, rows], lse[b, h, rows]
+        err = np.abs(got_o - O)
+        bound = tol_o + bf16_half_ulp(O)
+        assert np.all(err <= bound), (b, h, float(err.max()), float(np.max(err - bound)))
+        el = max_abs(got_l, L)
+        assert el <= tol_l, (b, h, el)
+        report.append((b, h, float(err.max()), el))
+    return report
+
+
+def _full_output_properties(w, inp, o, lse):
+    """Checks over every output element, at any size: finite; each output row
+    is a convex combination of value rows (within bf16 rounding); for causal
+    rows, LSE_i >= the score with key 0 and with key i."""
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    G = w.H_q // w.H_kv
+    v = inp.f64("v")
+    q = inp.f64("q")
+    k = inp.f64("k")
+    s = oracle.fp32_scale(w.scale)
+    for b in range(w.B):
+        for h in range(w.H_q):
+            hk = h // G
+            # P is rounded to bf16 before the P V product and O is stored in
+            # bf16: allow 2^-7 relative slack on top of the absolute tolerance.
+            slack = 1e-2 + 2.0 ** -7 * np.abs(v[b, hk]).max()
+            vmin = v[b, hk].min(axis=0) - slack
+            vmax = v[b, hk].max(axis=0) + slack
+            assert np.all(o[b, h] >= vmin) and np.all(o[b, h] <= vmax)
+            s0 = s * (q[b, h] @ k[b, hk, 0])
+            assert np.all(lse[b, h] >= s0 - 1e-3)
+            if w.causal and w.N_kv >= w.N_q:
+                sii = s * np.einsum("nd,nd->n", q[b, h], k[b, hk, :w.N_q])
+                assert np.all(lse[b, h] >= sii - 1e-3)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4x"])
+def test_config_parity(name):
+    w = WORKLOADS[name]
+    print(f"config {name}: {w}", flush=True)
+    inp = make_inputs(w)
+    o, lse = run_fwd(inp, w.causal, w.scale)
+    rng = np.random.default_rng(w.seed)
+    tol = TOL[w.dtype]
+    if name == "c1":
+        O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.causal, w.scale)
+        assert max_abs(o, O) <= tol["o"] and max_abs(lse, L) <= tol["lse"]
+        print(f"c1 max-abs O {max_abs(o, O):.3e} LSE {max_abs(lse, L):.3e}")
+        return
+    heads = sorted({(0, 0), (w.B - 1, w.H_q - 1), (0, w.H_q // 2), (w.B - 1, 1 % w.H_q)})
+    rep = _row_sample_check(w, inp, o, lse, rng, heads, tol["o"], tol["lse"])
+    print(f"{name} sampled rows: {rep}")
+    _full_output_properties(w, inp, o, lse)
+
+
+def test_q_zero_closed_form_full_size():
+    """Q = 0 makes every row uniform over its allowed keys (c3 shape)."""
+    import torch
+    import exact_attention_109_amd as fa
+    w = WORKLOADS["c3"]
+    inp = make_inputs(w)
+    q, k, v = upload(inp)
+    q.zero_()
+    o, lse = fa.fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    V = inp.f64("v")
+    n = np.arange(1, w.N_q + 1)
+    assert max_abs(lse, np.broadcast_to(np.log(n), lse.shape)) <= 1e-3
+    for (b, h) in [(0, 0), (1, 31)]:
+        mean = np.cumsum(V[b, h], axis=0) / n[:, None]
+        assert max_abs(o[b, h], mean) <= 1e-2
+
+
+def test_determinism():
+    import torch
+    import exact_attention_109_amd as fa
+    inp = make_inputs_shape(DTYPE_BF16, 2, 8, 2, 1000, 1000, 128, seed=33)
+    q, k, v = upload(inp)
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
