@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times (HBM "
+                         "counter calibration for the traffic figure) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -112,6 +115,16 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.load_library()
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
+        return
 
     w = WORKLOADS[args.workload]
     print(f"# workload {w}", file=sys.stderr, flush=True)

@@ -10,25 +10,36 @@
 //
 // gfx950 mapping
 // --------------
-//  * Workgroup = 4 wave64s, 128 query rows (32 per wave). One workgroup per
-//    (batch, query head, 128-row tile); grid order puts the heaviest causal
-//    tiles first and keeps all tiles of one key/value head on one XCD.
+//  * Workgroup = 8 wave64s, 256 query rows (32 per wave), one workgroup per
+//    CU (2 waves per SIMD). One workgroup per (batch, query head, 256-row
+//    tile); grid order puts the heaviest causal tiles first and keeps all
+//    tiles of one key/value head on one XCD.
 //  * Contractions on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The
 //    scores are computed transposed, S^T = K Q^T (K as the A operand, Q as B),
 //    so that a lane owns one query column; P^T then feeds O^T = V^T P^T as the
-//    B operand straight from the accumulator registers, and every per-row
-//    quantity (max, sum, rescale factor) is lane-local. The two halves of a
-//    wave hold disjoint keys of the same query and meet through one
-//    v_permlane32_swap.
-//  * K and V blocks come from HBM in 16-byte loads (prefetched one block
-//    ahead into registers) and are written to a double-buffered LDS: K as
-//    rows with XOR-swizzled 16-byte chunks, V transposed (4x8 register
-//    transpose) so that the V^T operand is one 16-byte LDS read per MFMA.
+//    B operand straight from registers, and every per-row quantity (max, sum,
+//    rescale factor) is lane-local. The two halves of a wave hold disjoint
+//    keys of the same query and meet through one v_permlane32_swap.
+//  * Ping-pong between the two waves of each SIMD: waves 0-3 (group A) and
+//    4-7 (group B) run the same per-block sequence -- an MFMA phase
+//    (PV of block j-1, then QK^T of block j) and a vector phase (mask, max,
+//    exponentials, row sums, bf16 packing of block j) -- with B one phase
+//    behind A, and a workgroup barrier at every phase boundary. At any time
+//    one wave of each SIMD drives the matrix core while its partner runs the
+//    softmax on the vector ALU.
+//  * K and V blocks stream from HBM straight into LDS with 16-byte
+//    global_load_lds_dwordx4 issued by group B during its vector phase
+//    (no register staging, double-buffered). Tiles are row-major with
+//    XOR-swizzled 16-byte chunks chosen so that every LDS read is free of bank
+//    conflicts. The V^T operand is read with ds_read_b64_tr_b16, which
+//    transposes 16-bit elements across lanes.
 //  * Softmax in base 2: scores are multiplied by scale*log2(e) inside one FMA
-//    and exponentiated with v_exp_f32; LSE is converted back with ln 2.
+//    and exponentiated with v_exp_f32; LSE is converted back with ln 2. The
+//    output rescale is skipped unless some row's max grew by more than 2^8
+//    (exact: the final division and the LSE use the same, possibly stale, max).
 //  * Causal: K/V blocks past the tile's last row are never loaded; waves whose
-//    rows all precede a block skip it; masking runs only on blocks that cross
-//    the diagonal or the end of the keys.
+//    rows all precede a block skip its work; masking runs only on blocks that
+//    cross the diagonal or the end of the keys.
 
 #include "fa_device.hpp"
 #include "fa_internal.h"
@@ -36,32 +47,67 @@
 namespace fa {
 namespace {
 
-constexpr int kBR = 128;     // query rows per workgroup
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;       // query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;  // log2 units: skip the rescale while max grows by <= 2^8
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;             // keys per block: 64 (d=128), 128 (d=64)
-  static constexpr int NSUB = BC / 32;            // 32-key subtiles of S^T
-  static constexpr int DSUB = D / 32;             // 32-column subtiles of O^T
-  static constexpr int QK_STEPS = D / 16;         // MFMA k-steps over the head dimension
-  static constexpr int PV_STEPS = BC / 16;        // MFMA k-steps over keys
-  static constexpr int KCHUNKS = D / 8;           // 16-byte chunks per K row
-  static constexpr int K_LOADS = BC * D / 8 / kThreads;  // K chunks per thread per block
-  static constexpr int TILE = BC * D;             // elements in one K or V^T buffer
+  static constexpr int BC = 8192 / D;              // keys per block: 64 (d=128), 128 (d=64)
+  static constexpr int NSUB = BC / 32;             // 32-key subtiles of S^T
+  static constexpr int DSUB = D / 32;              // 32-column subtiles of O^T
+  static constexpr int QK_STEPS = D / 16;          // MFMA k-steps over the head dimension
+  static constexpr int PV_STEPS = BC / 16;         // MFMA k-steps over keys
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;             // rows per 1 KiB LDS-DMA instruction
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BC * D * 2;    // 16 KiB
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;  // per tile, 4 loader waves
 };
 
-// K row r keeps chunk c at c ^ swz_k(r): the 8 rows read together by lanes
-// 8a..8a+7 of the S^T A operand get 8 distinct bank groups.
-__device__ __forceinline__ int swz_k(int r) { return (r & 3) | ((r >> 2) & 4); }
-// V^T row r (a head-dimension column of V) keeps key chunk c at c ^ swz_v(r).
-__device__ __forceinline__ int swz_v(int r) { return (r ^ (r >> 3)) & 7; }
+// Chunk swizzles (16-byte chunk index XOR f(row)).
+//  K: the 16 lanes of an S^T A-operand read phase touch 16 distinct rows at one
+//     logical chunk; f_k spreads them over all 16 (d=128) or 8 x 2-row (d=64)
+//     bank groups.
+//  V: a ds_read_b64_tr_b16 phase reads 4 consecutive rows x 64 bytes; f_v
+//     moves each of the 4 rows to a different 64-byte bank group.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return (row & 7) | ((row >> 1) & 8);
+  else return ((row >> 1) & 3) | ((row >> 2) & 4);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return (row & 3) << 2;
+  else return ((row >> 1) & 1) << 2;
+}
 
 // Key held by A-operand row m of a 32-key subtile. With this order the S^T
 // accumulator register i of lane half g holds key 16*g + i, so each lane's
 // probabilities come out as runs of 8 consecutive keys -- the layout of the
 // B operand of the P V contraction.
 __device__ __forceinline__ int key_of_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_AS void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
@@ -70,14 +116,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, float c) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vts[2][C::TILE];
+  constexpr int NSUB = C::NSUB;
+  // Four separate LDS objects (K and V, two buffers each) so that the compiler
+  // can tell the tiles being read from the ones the in-flight LDS DMA writes,
+  // and does not wait for the prefetch before every LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 31;   // query column of this lane (and MFMA row for A operands)
-  const int half = lane >> 5;  // lane half: key half for S^T, d half for the Q/K operands
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;    // 0: group A (leads), 1: group B (one phase behind, loads K/V)
+  const int gw = wave & 3;      // index within the group (= SIMD)
+  const int col = lane & 31;    // query column of this lane (and MFMA row for A operands)
+  const int half = lane >> 5;   // lane half: key half for S^T, d half for the Q/K operands
   const int G = H_q / H_kv;
 
   // ---- schedule: workgroup -> (batch, head, query tile)
@@ -107,8 +161,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const size_t qbase = (size_t(b) * H_q + h) * size_t(N_q) * D;
   const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
-  const uint16_t* __restrict__ Kh = K + kvbase;
-  const uint16_t* __restrict__ Vh = V + kvbase;
+  const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
+  const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
 
   // ---- Q tile into registers: B operand of S^T = K Q^T (read once)
   const int wrow0 = q0 + wave * 32;
@@ -120,174 +174,239 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int t = 0; t < C::QK_STEPS; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
   }
 
-  // ---- number of K/V blocks this workgroup visits
+  // ---- blocks visited by the workgroup (nblk) and computed by this wave (nact)
   const int nblk_all = (N_kv + BC - 1) / BC;
   int nblk = nblk_all;
   if (CAUSAL) {
     const int last_row = min(q0 + kBR, N_q) - 1;
     nblk = min(nblk_all, last_row / BC + 1);
   }
-  const int wlast = min(wrow0 + 31, N_q - 1);  // last valid row of this wave (< wrow0 if none)
-
-  // ---- staging of one K/V block: HBM -> registers -> LDS
-  u32x4 kpre[C::K_LOADS];
-  u32x4 vpre[4];
-  const int vkg = tid / (D / 8);  // V: 4-key group
-  const int vdg = tid % (D / 8);  // V: 8-column group
-
-  auto load_block = [&](int j) {
+  const int wlast = min(wrow0 + 31, N_q - 1);
+  int nact = 0;
+  if (wrow0 < N_q) nact = CAUSAL ? min(nblk, wlast / BC + 1) : nblk;
+  auto need_mask = [&](int j) __attribute__((always_inline)) {
     const int kv0 = j * BC;
+    return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
+  };
+
+  // ---- LDS-DMA staging by the 4 waves of group B: each fills DMA_PER_WAVE
+  // KiB of a tile. Instruction i writes bytes [1024*ig, 1024*ig + 1024) of the
+  // tile, lane l the 16 bytes at 16*l: row RPI*ig + l/CPR, physical chunk
+  // l%CPR, which holds logical chunk (l%CPR) ^ swz(row).
+  uint32_t dma_koff[C::DMA_PER_WAVE];
+  uint32_t dma_voff[C::DMA_PER_WAVE];
 #pragma unroll
-    for (int r = 0; r < C::K_LOADS; ++r) {
-      const int ci = tid + kThreads * r;
-      const int row = ci / C::KCHUNKS;
-      const int ch = ci % C::KCHUNKS;
-      const int krow = min(kv0 + row, N_kv - 1);
-      kpre[r] = ld_global16(Kh + size_t(krow) * D + ch * 8);
-    }
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int ig = gw * C::DMA_PER_WAVE + i;
+    const int row = C::RPI * ig + lane / C::CPR;
+    const int p = lane % C::CPR;
+    dma_koff[i] = row * C::ROW_BYTES + (p ^ swz_k<D>(row)) * 16;
+    dma_voff[i] = row * C::ROW_BYTES + (p ^ swz_v<D>(row)) * 16;
+  }
+  // One tile (K or V) of block j into LDS. Full blocks address from a uniform
+  // base plus a per-lane 32-bit offset; the last block clamps rows to N_kv-1.
+  auto dma_tile = [&](int j, const uint8_t* src, const uint32_t (&off)[C::DMA_PER_WAVE], uint8_t* dst)
+      __attribute__((always_inline)) {
+    const int kv0 = j * BC;
+    if (kv0 + BC <= N_kv) {
+      const uint8_t* base = src + size_t(kv0) * C::ROW_BYTES;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int vrow = min(kv0 + 4 * vkg + r, N_kv - 1);
-      vpre[r] = ld_global16(Vh + size_t(vrow) * D + vdg * 8);
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i)
+        lds_dma16(base + off[i], (LDS_AS void*)(dst + 1024 * (gw * C::DMA_PER_WAVE + i)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const int row = int(off[i] / C::ROW_BYTES);
+        const int grow = min(kv0 + row, N_kv - 1);
+        lds_dma16(src + size_t(grow) * C::ROW_BYTES + (off[i] % C::ROW_BYTES),
+                  (LDS_AS void*)(dst + 1024 * (gw * C::DMA_PER_WAVE + i)));
+      }
     }
   };
 
-  auto store_block = [&](int buf) {
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  // K (S^T A operand): row key_of_row(col) of subtile n (n adds 32 rows), chunk (D/16)*half + t.
+  const int krow = key_of_row(col);
+  int koff[C::QK_STEPS];
 #pragma unroll
-    for (int r = 0; r < C::K_LOADS; ++r) {
-      const int ci = tid + kThreads * r;
-      const int row = ci / C::KCHUNKS;
-      const int ch = ci % C::KCHUNKS;
-      st_lds16(ks[buf], row * D + ((ch ^ swz_k(row)) * 8), kpre[r]);
-    }
-    // 4 keys x 8 columns -> 8 columns x 4 keys
+  for (int t = 0; t < C::QK_STEPS; ++t)
+    koff[t] = krow * C::ROW_BYTES + ((((D / 16) * half + t) ^ swz_k<D>(krow)) * 16);
+  // V (O^T A operand via transposed reads): a 16-lane group j = lane%16 reads
+  // rows r0 + j/4 (r0 = 32n + 16*half + 8w + 4r) at columns c0 + 4*(j%4),
+  // c0 = 32*s + 16*((lane%32)/16).
+  const int j16 = lane & 15;
+  const int vgrp = (lane & 31) >> 4;
+  int voff[C::DSUB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      const uint32_t x0 = (vpre[0][w] >> sh) & 0xffffu;
-      const uint32_t x1 = (vpre[1][w] >> sh) & 0xffffu;
-      const uint32_t x2 = (vpre[2][w] >> sh) & 0xffffu;
-      const uint32_t x3 = (vpre[3][w] >> sh) & 0xffffu;
-      u32x2 packed;
-      packed[0] = x0 | (x1 << 16);
-      packed[1] = x2 | (x3 << 16);
-      const int row = 8 * vdg + e;
-      st_lds8(vts[buf], row * BC + (((vkg >> 1) ^ swz_v(row)) * 8) + (vkg & 1) * 4, packed);
-    }
-  };
+  for (int s = 0; s < C::DSUB; ++s) {
+    const int row = 16 * half + (j16 >> 2);
+    const int cc = 32 * s + 16 * vgrp + 4 * (j16 & 3);
+    voff[s] = row * C::ROW_BYTES + (((cc >> 3) ^ swz_v<D>(row)) * 16) + (cc & 7) * 2;
+  }
 
-  // ---- online-softmax state (per query column, identical in both lane halves
-  // except l, which each half accumulates over its own keys)
+  // ---- online-softmax state (per query column; l is per lane half)
   float m_run = -INFINITY;
   float l_run = 0.f;
   f32x16 oacc[C::DSUB];
 #pragma unroll
   for (int s = 0; s < C::DSUB; ++s) oacc[s] = f32x16{};
+  f32x16 sacc[NSUB];          // scores of the current block
+  u32x4 pk[C::PV_STEPS];      // its probabilities, bf16-packed as PV B operands
 
-  const int krow_a = key_of_row(col);
-
-  load_block(0);
-  store_block(0);
-  __syncthreads();
-
-  for (int j = 0; j < nblk; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nblk) load_block(j + 1);
-    const int kv0 = j * BC;
-    const bool active = (wrow0 < N_q) && (!CAUSAL || kv0 <= wlast);
-    if (active) {
-      // S^T = K_j Q^T
-      f32x16 sacc[C::NSUB];
+  // MFMA phase for block j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
+  auto pv_part = [&](const uint8_t* vt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int n = 0; n < C::NSUB; ++n) sacc[n] = f32x16{};
+    for (int u = 0; u < C::PV_STEPS; ++u) {
+      const int rbase = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;  // + 4 rows for the second read
 #pragma unroll
-      for (int t = 0; t < C::QK_STEPS; ++t) {
-#pragma unroll
-        for (int n = 0; n < C::NSUB; ++n) {
-          const int row = 32 * n + krow_a;
-          const int ch = half * (D / 16) + t;
-          const bf16x8 a = as_bf16x8(ld_lds16(ks[buf], row * D + ((ch ^ swz_k(row)) * 8)));
-          sacc[n] = mfma32x32x16(a, qreg[t], sacc[n]);
-        }
+      for (int s = 0; s < C::DSUB; ++s) {
+        LDS_AS i16x4* p0 = (LDS_AS i16x4*)(vt + voff[s] + rbase);
+        LDS_AS i16x4* p1 = (LDS_AS i16x4*)(vt + voff[s] + rbase + 4 * C::ROW_BYTES);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+        u32x4 av;
+        av[0] = __builtin_bit_cast(u32x2, lo)[0];
+        av[1] = __builtin_bit_cast(u32x2, lo)[1];
+        av[2] = __builtin_bit_cast(u32x2, hi)[0];
+        av[3] = __builtin_bit_cast(u32x2, hi)[1];
+        oacc[s] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pk[u]), oacc[s]);
       }
-      // mask: causal diagonal and the end of the keys. Masked scores become
-      // -inf for the max and their probabilities are forced to 0 below (an
-      // exp2 of -inf * c would be NaN for scale == 0).
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
-      uint32_t mbits[C::NSUB];
-      if (need_mask) {
+    }
+  };
+  auto qk_part = [&](const uint8_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < C::NSUB; ++n) {
-          mbits[n] = 0;
+    for (int n = 0; n < NSUB; ++n) sacc[n] = f32x16{};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * n + 16 * half + i;
-            const bool masked = (CAUSAL && key > qrow) || key >= N_kv;
-            if (masked) {
-              sacc[n][i] = -INFINITY;
-              mbits[n] |= 1u << i;
-            }
-          }
-        }
+    for (int t = 0; t < C::QK_STEPS; ++t) {
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[t] + n * 32 * C::ROW_BYTES));
+        sacc[n] = mfma32x32x16(a, qreg[t], sacc[n]);
       }
-      // row max over the block (in-lane, then across the two halves)
-      float mx = sacc[0][0];
+    }
+  };
+  // Operand reads run ahead of the MFMAs that consume them: 8 V reads up
+  // front, then 2 reads behind every PV MFMA and 1 behind every QK^T MFMA
+  // (the K reads of the QK^T part start while the last PV MFMAs run).
+  auto pv_schedule = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int n = 0; n < C::NSUB; ++n)
+    for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
+    for (int i = 0; i < C::PV_STEPS * C::DSUB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    }
+  };
+  auto qk_schedule = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int n = 0; n < C::NSUB; ++n) {
+    for (int i = 0; i < C::QK_STEPS * NSUB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+  };
+  auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    const bool do_pv = j >= 1 && j - 1 < nact;
+    const bool do_qk = j < nact;
+    if (do_pv) {
+      pv_part(vt);
+      pv_schedule();
+    }
+    if (do_qk) {
+      qk_part(kt);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      qk_schedule();
+    }
+  };
+
+  // Vector phase for block j: mask, block max, (rare) rescale, exponentials,
+  // row sums and bf16 packing.
+  auto valu_phase = [&](int j) __attribute__((always_inline)) {
+    if (j < 0 || j >= nact) return;
+    if (need_mask(j)) {
+      const int kv0 = j * BC;
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[n][i], c, -m_new));
-          sacc[n][i] = p;
-          psum += p;
+          const int key = kv0 + 32 * n + 16 * half + i;
+          if ((CAUSAL && key > qrow) || key >= N_kv) sacc[n][i] = -INFINITY;
         }
-      }
-      if (need_mask) {
-        psum = 0.f;
+    }
+    float mx = sacc[0][0];
 #pragma unroll
-        for (int n = 0; n < C::NSUB; ++n)
+    for (int n = 0; n < NSUB; ++n)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (mbits[n] & (1u << i)) sacc[n][i] = 0.f;
-            psum += sacc[n][i];
-          }
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
+    const float m_blk = max_xor32(mx) * c;
+    if (__any(m_blk > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int s = 0; s < C::DSUB; ++s)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
-      // O^T += V_j^T P^T
-#pragma unroll
-      for (int u = 0; u < C::PV_STEPS; ++u) {
-        const int n = u >> 1;
-        const int w8 = (u & 1) * 8;
-        u32x4 pk;
-        pk[0] = pack_bf16x2(sacc[n][w8 + 0], sacc[n][w8 + 1]);
-        pk[1] = pack_bf16x2(sacc[n][w8 + 2], sacc[n][w8 + 3]);
-        pk[2] = pack_bf16x2(sacc[n][w8 + 4], sacc[n][w8 + 5]);
-        pk[3] = pack_bf16x2(sacc[n][w8 + 6], sacc[n][w8 + 7]);
-        const bf16x8 pb = as_bf16x8(pk);
-        const int ch = 4 * n + 2 * half + (u & 1);
-#pragma unroll
-        for (int s = 0; s < C::DSUB; ++s) {
-          const int row = 32 * s + col;
-          const bf16x8 a = as_bf16x8(ld_lds16(vts[buf], row * BC + ((ch ^ swz_v(row)) * 8)));
-          oacc[s] = mfma32x32x16(a, pb, oacc[s]);
-        }
-      }
+      m_run = m_new;
     }
-    if (j + 1 < nblk) store_block(buf ^ 1);
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < C::PV_STEPS; ++u) {
+      const int n = u >> 1;
+      const int w8 = (u & 1) * 8;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(sacc[n][w8 + e], c, -m_run));
+        psum += p[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+    }
+    l_run += psum;
+  };
+
+  // Two phases (ticks) per block j. Group A: MFMA(j) | VALU(j).
+  // Group B: VALU(j-1) + DMA of K_{j+1}, V_j | MFMA(j), then wait for the DMA.
+  // Buffers: K_j in kb[j%2], V_j in vb[j%2]. Each group runs its own loop
+  // (the group test is outside the loop, so the compiler never has to keep
+  // both groups' register state alive across the barriers); both loops pass
+  // the same 2*(nblk+1) barriers.
+  auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
+    mfma_phase(j, k_cur, v_prev);
     __syncthreads();
+    valu_phase(j);
+    __syncthreads();
+  };
+  auto block_b = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev, uint8_t* k_dma, uint8_t* v_dma)
+      __attribute__((always_inline)) {
+    valu_phase(j - 1);
+    if (j + 1 < nblk) dma_tile(j + 1, Kbytes, dma_koff, k_dma);
+    if (j < nblk) dma_tile(j, Vbytes, dma_voff, v_dma);
+    __syncthreads();
+    mfma_phase(j, k_cur, v_prev);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  // ---- prologue: K_0 into kb0
+  if (grp == 1) {
+    dma_tile(0, Kbytes, dma_koff, kb0);
+    wait_vmem();
+  }
+  __syncthreads();
+
+  // Blocks 0..nblk: the extra step j = nblk finishes PV of the last block.
+  if (grp == 0) {
+    for (int j = 0; j <= nblk; j += 2) {
+      block_a(j, kb0, vb1);
+      if (j + 1 <= nblk) block_a(j + 1, kb1, vb0);
+    }
+  } else {
+    for (int j = 0; j <= nblk; j += 2) {
+      block_b(j, kb0, vb1, kb1, vb0);
+      if (j + 1 <= nblk) block_b(j + 1, kb1, vb0, kb0, vb1);
+    }
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
@@ -300,8 +419,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         u32x2 w;
-        w[0] = pack_bf16x2(oacc[s][4 * a + 0] * inv, oacc[s][4 * a + 1] * inv);
-        w[1] = pack_bf16x2(oacc[s][4 * a + 2] * inv, oacc[s][4 * a + 3] * inv);
+        w[0] = cvt_pk_bf16(oacc[s][4 * a + 0] * inv, oacc[s][4 * a + 1] * inv);
+        w[1] = cvt_pk_bf16(oacc[s][4 * a + 2] * inv, oacc[s][4 * a + 3] * inv);
         st_global8(op + 32 * s + 8 * a + 4 * half, w);
       }
     }
@@ -314,7 +433,10 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int n_qtiles = (p.N_q + kBR - 1) / kBR;
   const long long nwg = (long long)n_qtiles * p.B * p.H_q;
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
-  const float c = p.scale * kLog2e;
+  // Masked scores are -inf and exp2(-inf * c) must be 0, so c stays positive:
+  // for scale == 0 the smallest normal float gives exactly the uniform weights
+  // (every unmasked exponent rounds to exp2(0) = 1).
+  const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<uint16_t*>(p.o), p.lse,
