@@ -90,6 +90,32 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
     }
 
 
+def time_backward(fa, torch, steps: int, warmup: int):
+    """fa_bwd (pre + dK/dV + dQ kernels) on the c5 workload, inputs and the
+    forward's O/LSE resident in HBM."""
+    w = WORKLOADS["c5"]
+    inp = make_inputs(w)
+    q, k, v, do = (inp.torch(n, "cuda") for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    ws = torch.empty((fa.fa_bwd_workspace_size(w.B, w.H_q, w.N_q),), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"workload": w.name, "ms_per_call": round(ms, 4),
+            "tflops_2p5x_convention": round(w.bwd_flop / (ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(w.bwd_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "FLOP = 2.5 x forward FLOP; the kernels issue 3.5 x (S, dP recomputed in both passes)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +124,7 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement on c5")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
@@ -190,6 +217,9 @@ def main():
                    "arch": getattr(props, "gcnArchName", "")},
         "wall_s_timed_region": round(wall, 3),
     }
+    if not args.no_bwd:
+        print("# timing the backward on c5", file=sys.stderr, flush=True)
+        result["bwd"] = time_backward(fa, torch, max(3, args.steps // 2), 2)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

@@ -111,7 +111,8 @@ FA_EXPORT int fa_fwd(const void* q, const void* k, const void* v, void* o, float
 
 FA_EXPORT size_t fa_bwd_workspace_size(int B, int H_q, int N_q) {
   if (B <= 0 || H_q <= 0 || N_q <= 0) return 0;
-  size_t bytes = size_t(B) * H_q * N_q * sizeof(float);
+  // two float32 values per query row: D_i = <dO_i, O_i> and lse_i * log2(e)
+  size_t bytes = 2 * size_t(B) * H_q * N_q * sizeof(float);
   return (bytes + 255) & ~size_t(255);
 }
 

@@ -1,10 +1,529 @@
-// Attention backward for bf16 inputs: dispatch.
+// Attention backward for bf16 inputs on gfx950 (MI355X), by recomputation.
+//
+// "Flash-Attention" (Awesome System Papers Wiki), core-idea section: the
+// backward pass does not keep the N x N probability matrix; it rebuilds the
+// probabilities from Q, K, V and per-row statistics saved by the forward
+// pass, trading extra arithmetic for memory and HBM traffic. With
+// P_ij = exp(scale * q_i.k_j - lse_i) over the allowed keys:
+//     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   D_i = <dO_i, O_i>
+//     dQ = scale * dS K,   dK = scale * dS^T Q
+// (textbook derivatives of the forward definition; the pages give none).
+//
+// Three kernels on one stream, no atomics (deterministic):
+//  * pre:  D_i and lse_i*log2(e) for every query row (HBM-bound pass over O, dO).
+//  * dkdv: one workgroup per (batch, key/value head, 128-key tile); each wave
+//          owns 32 keys and keeps their K and V as MFMA operands in
+//          registers, while the query blocks of every query head of the
+//          group stream past through LDS. Per 64-query block and wave:
+//          S = Q K^T and dP = dO V^T (queries x keys, Q/dO rows read from LDS),
+//          P and dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
+//          dO/Q operands read transposed (ds_read_b64_tr_b16).
+//  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
+//          owns 32 queries (Q and dO as register operands) while the K/V
+//          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
+//          dQ^T += K^T dS^T with K read transposed.
+// The accumulator layouts are arranged so that P and dS leave the MFMA
+// accumulators already in the k-layout of the next contraction's B operand
+// (see row_of_lane), and every LDS tile uses one XOR swizzle that is free of
+// bank conflicts for both its row reads and its transposed reads.
+
+#include "fa_device.hpp"
 #include "fa_internal.h"
 
 namespace fa {
+namespace {
 
-hipError_t launch_bwd_bf16_valu(const BwdParams& p, hipStream_t stream);
+constexpr int kThreads = 256;
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) { return launch_bwd_bf16_valu(p, stream); }
+// 16-byte chunk swizzle shared by the row reads (16 lanes read the rows
+// row_of_lane(0..15) at one logical chunk) and the transposed reads (a phase
+// reads 4 consecutive rows x 64 bytes) of a bf16 tile.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 1) | ((row >> 3) & 2);
+  else return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1);
+}
+
+template <int D>
+struct BwdCfg {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows per 1 KiB LDS-DMA instruction
+  static constexpr int KST = D / 16;         // MFMA k-steps over the head dimension
+  static constexpr int DSUB = D / 32;        // 32-column output subtiles
+  static constexpr int BLK = 64;             // rows (queries or keys) per streamed block
+  static constexpr int NSUB = BLK / 32;      // 32-row subtiles of a block
+  static constexpr int STEPS = BLK / 16;     // MFMA k-steps over a block
+  static constexpr int TILE_BYTES = BLK * D * 2;
+  static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;
+};
+
+// Per-lane byte offsets of the LDS-DMA writes of one tile (this wave's
+// share): row RPI*ig + l/CPR, physical chunk l%CPR = logical chunk ^ swz(row).
+template <int D>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[BwdCfg<D>::DMA_PER_WAVE]) {
+  using C = BwdCfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+    const int ig = wave * C::DMA_PER_WAVE + i;
+    const int row = C::RPI * ig + lane / C::CPR;
+    const int p = lane % C::CPR;
+    off[i] = row * C::ROW_BYTES + (p ^ swz<D>(row)) * 16;
+  }
+}
+
+// Rows [r0, r0 + BLK) of a row-major [rows][D] bf16 matrix into an LDS tile;
+// rows past `nrows` repeat the last row (their results are masked).
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint8_t* src, int r0, int nrows,
+                                         const uint32_t (&off)[BwdCfg<D>::DMA_PER_WAVE], uint8_t* dst, int wave) {
+  using C = BwdCfg<D>;
+  if (r0 + C::BLK <= nrows) {
+    const uint8_t* base = src + size_t(r0) * C::ROW_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i)
+      lds_dma16(base + off[i], (LDS_AS void*)(dst + 1024 * (wave * C::DMA_PER_WAVE + i)));
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int row = int(off[i] / C::ROW_BYTES);
+      const int grow = min(r0 + row, nrows - 1);
+      lds_dma16(src + size_t(grow) * C::ROW_BYTES + (off[i] % C::ROW_BYTES),
+                (LDS_AS void*)(dst + 1024 * (wave * C::DMA_PER_WAVE + i)));
+    }
+  }
+}
+
+// Per-lane offsets for the row reads (A operand with rows row_of_lane(col),
+// chunk (D/16)*half + t; subtile n adds 32 rows) and the transposed reads
+// (rows 16*half + j/4 + 4r, columns 32s + 16*((lane%32)/16) + 4*(j%4),
+// j = lane%16; block step u adds 32*(u/2) + 8*(u%2) rows).
+template <int D>
+struct ReadOffsets {
+  int row[BwdCfg<D>::KST];
+  int tr[BwdCfg<D>::DSUB][2];
+  __device__ __forceinline__ void init(int lane) {
+    using C = BwdCfg<D>;
+    const int col = lane & 31, half = lane >> 5;
+    const int r = row_of_lane(col);
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) row[t] = r * C::ROW_BYTES + ((((D / 16) * half + t) ^ swz<D>(r)) * 16);
+    const int j16 = lane & 15, vgrp = (lane & 31) >> 4;
+#pragma unroll
+    for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int tr_row = 16 * half + (j16 >> 2) + 4 * q;
+        const int cc = 32 * s + 16 * vgrp + 4 * (j16 & 3);
+        tr[s][q] = tr_row * C::ROW_BYTES + (((cc >> 3) ^ swz<D>(tr_row)) * 16) + (cc & 7) * 2;
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// pre: D_i = <dO_i, O_i>, L2_i = lse_i * log2(e)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ LSE, float* __restrict__ Dl,
+                                                           float* __restrict__ L2, long long rows) {
+  constexpr int TPR = D / 8;                // threads per row, 8 elements (16 bytes) each
+  constexpr int RPB = kThreads / TPR;       // rows per workgroup
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / TPR;
+  const int part = tid % TPR;
+  const long long rc = row < rows ? row : rows - 1;
+  const u32x4 o = ld_global16(O + rc * D + part * 8);
+  const u32x4 g = ld_global16(dO + rc * D + part * 8);
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    acc = fmaf(__uint_as_float(o[w] << 16), __uint_as_float(g[w] << 16), acc);
+    acc = fmaf(__uint_as_float(o[w] & 0xffff0000u), __uint_as_float(g[w] & 0xffff0000u), acc);
+  }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && part == 0) {
+    Dl[row] = acc;
+    L2[row] = LSE[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+constexpr int kKeysPerWg = 128;  // 4 waves x 32 keys
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
+    float* __restrict__ dK, float* __restrict__ dV, int H_q, int H_kv, int N_q, int N_kv, int n_ktiles,
+    int xcd_remap, float c, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int BQ = C::BLK;
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t os0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t os1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float ls0[BQ];
+  __shared__ __attribute__((aligned(256))) float ls1[BQ];
+  __shared__ __attribute__((aligned(256))) float ds0[BQ];
+  __shared__ __attribute__((aligned(256))) float ds1[BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int G = H_q / H_kv;
+
+  // key tiles: the first ones see the most queries when causal, so they go first
+  const TileAssign ta = assign_tile(blockIdx.x, n_ktiles, 1, xcd_remap);
+  const int b = ta.kvidx / H_kv;
+  const int hk = ta.kvidx % H_kv;
+  const int k0 = ta.tile_rank * kKeysPerWg;
+  const int kw = k0 + 32 * wave;   // first key of this wave
+  const int key = kw + col;        // this lane's key (MFMA column)
+
+  const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+  // K and V of this wave's 32 keys as B operands (k = head dimension)
+  bf16x8 kreg[C::KST], vreg[C::KST];
+  {
+    const size_t off = kvbase + size_t(min(key, N_kv - 1)) * D + half * (D / 2);
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) {
+      kreg[t] = as_bf16x8(ld_global16(K + off + 8 * t));
+      vreg[t] = as_bf16x8(ld_global16(V + off + 8 * t));
+    }
+  }
+
+  // query blocks: for each of the G query heads, blocks from qstart to N_q
+  const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int nqb = qstart < N_q ? (N_q - qstart + BQ - 1) / BQ : 0;
+  const int nblk = G * nqb;
+
+  uint32_t dma_off[C::DMA_PER_WAVE];
+  dma_offsets<D>(wave, lane, dma_off);
+  ReadOffsets<D> ro;
+  ro.init(lane);
+
+  auto block_head = [&](int jb, int& h, int& qb0) __attribute__((always_inline)) {
+    const int g = jb / nqb;
+    h = hk * G + g;
+    qb0 = qstart + (jb % nqb) * BQ;
+  };
+  // Q and dO rows of block jb into LDS, plus its L2 and D vectors (64 floats each).
+  auto issue = [&](int jb, uint8_t* qd, uint8_t* od, float* ld, float* dd) __attribute__((always_inline)) {
+    int h, qb0;
+    block_head(jb, h, qb0);
+    const size_t rbase = (size_t(b) * H_q + h) * size_t(N_q);
+    dma_tile<D>(reinterpret_cast<const uint8_t*>(Q + rbase * D), qb0, N_q, dma_off, qd, wave);
+    dma_tile<D>(reinterpret_cast<const uint8_t*>(dO + rbase * D), qb0, N_q, dma_off, od, wave);
+    if (wave == 0) lds_dma4(L2 + rbase + min(qb0 + lane, N_q - 1), (LDS_AS void*)ld);
+    if (wave == 1) lds_dma4(Dl + rbase + min(qb0 + lane, N_q - 1), (LDS_AS void*)dd);
+  };
+
+  f32x16 dk[C::DSUB], dv[C::DSUB];
+#pragma unroll
+  for (int s = 0; s < C::DSUB; ++s) {
+    dk[s] = f32x16{};
+    dv[s] = f32x16{};
+  }
+
+  auto compute = [&](int jb, const uint8_t* qt, const uint8_t* ot, const float* lt, const float* dt)
+      __attribute__((always_inline)) {
+    int h, qb0;
+    block_head(jb, h, qb0);
+    (void)h;
+    if (CAUSAL && qb0 + BQ - 1 < kw) return;  // every query precedes every key of this wave
+    // S = Q K^T and dP = dO V^T (queries x keys; lane = key, register i of
+    // subtile n = query 32n + 16*half + i)
+    f32x16 sacc[C::NSUB], pacc[C::NSUB];
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n) {
+      sacc[n] = f32x16{};
+      pacc[n] = f32x16{};
+    }
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) {
+#pragma unroll
+      for (int n = 0; n < C::NSUB; ++n) {
+        const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
+        sacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o)), kreg[t], sacc[n]);
+        pacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o)), vreg[t], pacc[n]);
+      }
+    }
+    // P = exp2(S*c - L2_q), dS = P (dP - D_q); masked entries are 0
+    const bool need_mask = (CAUSAL && qb0 < kw + 31) || (qb0 + BQ > N_q);
+    u32x4 pk[C::STEPS], sk[C::STEPS];
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n) {
+      float l2v[16], dlv[16];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 32 * n + 16 * half + 4 * v4);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(dt + 32 * n + 16 * half + 4 * v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2v[4 * v4 + e] = a[e];
+          dlv[4 * v4 + e] = d[e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(sacc[n][i], c, -l2v[i]));
+        if (need_mask) {
+          const int q = qb0 + 32 * n + 16 * half + i;
+          if ((CAUSAL && key > q) || q >= N_q) p = 0.f;
+        }
+        sacc[n][i] = p;
+        pacc[n][i] = p * (pacc[n][i] - dlv[i]);
+      }
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pk[2 * n + w][e] = cvt_pk_bf16(sacc[n][8 * w + 2 * e], sacc[n][8 * w + 2 * e + 1]);
+          sk[2 * n + w][e] = cvt_pk_bf16(pacc[n][8 * w + 2 * e], pacc[n][8 * w + 2 * e + 1]);
+        }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys; dO/Q read transposed)
+#pragma unroll
+    for (int u = 0; u < C::STEPS; ++u) {
+      const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
+#pragma unroll
+      for (int s = 0; s < C::DSUB; ++s) {
+        const bf16x8 ao = lds_read_tr8(ot + ro.tr[s][0] + rb, ot + ro.tr[s][1] + rb);
+        dv[s] = mfma32x32x16(ao, as_bf16x8(pk[u]), dv[s]);
+        const bf16x8 aq = lds_read_tr8(qt + ro.tr[s][0] + rb, qt + ro.tr[s][1] + rb);
+        dk[s] = mfma32x32x16(aq, as_bf16x8(sk[u]), dk[s]);
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    issue(0, qs0, os0, ls0, ds0);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int jb = 0; jb < nblk; jb += 2) {
+    if (jb + 1 < nblk) issue(jb + 1, qs1, os1, ls1, ds1);
+    compute(jb, qs0, os0, ls0, ds0);
+    wait_vmem();
+    __syncthreads();
+    if (jb + 1 < nblk) {
+      if (jb + 2 < nblk) issue(jb + 2, qs0, os0, ls0, ds0);
+      compute(jb + 1, qs1, os1, ls1, ds1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // dK^T / dV^T accumulators: lane = key, register 4a+b of subtile s = column 32s + 8a + 4*half + b
+  if (key < N_kv) {
+    float* dkp = dK + kvbase + size_t(key) * D;
+    float* dvp = dV + kvbase + size_t(key) * D;
+#pragma unroll
+    for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 vk, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vk[e] = dk[s][4 * a + e] * scale;
+          vv[e] = dv[s][4 * a + e];
+        }
+        *reinterpret_cast<f32x4*>(dkp + 32 * s + 8 * a + 4 * half) = vk;
+        *reinterpret_cast<f32x4*>(dvp + 32 * s + 8 * a + 4 * half) = vv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+constexpr int kQueriesPerWg = 128;  // 4 waves x 32 queries
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
+    float* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, float c,
+    float scale) {
+  using C = BwdCfg<D>;
+  constexpr int BK = C::BLK;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int G = H_q / H_kv;
+
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap);
+  const int b = ta.kvidx / H_kv;
+  const int hk = ta.kvidx % H_kv;
+  const int h = hk * G + ta.gq;
+  const int tile = CAUSAL ? (n_qtiles - 1 - ta.tile_rank) : ta.tile_rank;  // heaviest first
+  const int q0 = tile * kQueriesPerWg;
+  const int wq0 = q0 + 32 * wave;
+  const int query = wq0 + col;  // this lane's query (MFMA column)
+
+  const size_t rbase = (size_t(b) * H_q + h) * size_t(N_q);
+  const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+  const int qc = min(query, N_q - 1);
+  bf16x8 qreg[C::KST], oreg[C::KST];
+  {
+    const size_t off = (rbase + qc) * D + half * (D / 2);
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) {
+      qreg[t] = as_bf16x8(ld_global16(Q + off + 8 * t));
+      oreg[t] = as_bf16x8(ld_global16(dO + off + 8 * t));
+    }
+  }
+  const float l2 = L2[rbase + qc];
+  const float dl = Dl[rbase + qc];
+
+  const int nblk_all = (N_kv + BK - 1) / BK;
+  int nblk = nblk_all;
+  if (CAUSAL) nblk = min(nblk_all, (min(q0 + kQueriesPerWg, N_q) - 1) / BK + 1);
+  const int wlast = min(wq0 + 31, N_q - 1);
+  int nact = 0;
+  if (wq0 < N_q) nact = CAUSAL ? min(nblk, wlast / BK + 1) : nblk;
+
+  uint32_t dma_off[C::DMA_PER_WAVE];
+  dma_offsets<D>(wave, lane, dma_off);
+  ReadOffsets<D> ro;
+  ro.init(lane);
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + kvbase);
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + kvbase);
+
+  f32x16 dq[C::DSUB];
+#pragma unroll
+  for (int s = 0; s < C::DSUB; ++s) dq[s] = f32x16{};
+
+  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    if (j >= nact) return;
+    const int kv0 = j * BK;
+    // S^T = K Q^T, dP^T = V dO^T (keys x queries; lane = query, register i of
+    // subtile n = key 32n + 16*half + i)
+    f32x16 sacc[C::NSUB], pacc[C::NSUB];
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n) {
+      sacc[n] = f32x16{};
+      pacc[n] = f32x16{};
+    }
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) {
+#pragma unroll
+      for (int n = 0; n < C::NSUB; ++n) {
+        const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
+        sacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o)), qreg[t], sacc[n]);
+        pacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vt + o)), oreg[t], pacc[n]);
+      }
+    }
+    const bool need_mask = (CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv);
+    u32x4 sk[C::STEPS];
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(sacc[n][i], c, -l2));
+        if (need_mask) {
+          const int kk = kv0 + 32 * n + 16 * half + i;
+          if ((CAUSAL && kk > query) || kk >= N_kv) p = 0.f;
+        }
+        pacc[n][i] = p * (pacc[n][i] - dl);
+      }
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sk[2 * n + w][e] = cvt_pk_bf16(pacc[n][8 * w + 2 * e], pacc[n][8 * w + 2 * e + 1]);
+    }
+    // dQ^T += K^T dS^T (d x queries; K read transposed)
+#pragma unroll
+    for (int u = 0; u < C::STEPS; ++u) {
+      const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
+#pragma unroll
+      for (int s = 0; s < C::DSUB; ++s) {
+        const bf16x8 a = lds_read_tr8(kt + ro.tr[s][0] + rb, kt + ro.tr[s][1] + rb);
+        dq[s] = mfma32x32x16(a, as_bf16x8(sk[u]), dq[s]);
+      }
+    }
+  };
+
+  dma_tile<D>(Kb, 0, N_kv, dma_off, ks0, wave);
+  dma_tile<D>(Vb, 0, N_kv, dma_off, vs0, wave);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < nblk; j += 2) {
+    if (j + 1 < nblk) {
+      dma_tile<D>(Kb, (j + 1) * BK, N_kv, dma_off, ks1, wave);
+      dma_tile<D>(Vb, (j + 1) * BK, N_kv, dma_off, vs1, wave);
+    }
+    compute(j, ks0, vs0);
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nblk) {
+      if (j + 2 < nblk) {
+        dma_tile<D>(Kb, (j + 2) * BK, N_kv, dma_off, ks0, wave);
+        dma_tile<D>(Vb, (j + 2) * BK, N_kv, dma_off, vs0, wave);
+      }
+      compute(j + 1, ks1, vs1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (query < N_q) {
+    float* dqp = dQ + (rbase + query) * D;
+#pragma unroll
+    for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dq[s][4 * a + e] * scale;
+        *reinterpret_cast<f32x4*>(dqp + 32 * s + 8 * a + 4 * half) = v;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdParams& p, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.H_q * p.N_q;
+  float* Dl = p.delta;
+  float* L2 = p.delta + rows;
+  constexpr int RPB = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.dO), p.lse, Dl, L2, rows);
+  // c > 0 keeps exp2(-inf)-style masking well defined; scale == 0 gives 1/count weights via the LSE
+  const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
+  const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
+  const int n_ktiles = (p.N_kv + kKeysPerWg - 1) / kKeysPerWg;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_ktiles * p.B * p.H_kv)),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                     static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dk, p.dv,
+                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_ktiles, xcd_remap, c, p.scale);
+  const int n_qtiles = (p.N_q + kQueriesPerWg - 1) / kQueriesPerWg;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_qtiles * p.B * p.H_q)), dim3(kThreads),
+                     0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                     static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dq, p.H_q,
+                     p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c, p.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  if (p.d == 128) return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+}
 
 }  // namespace fa

@@ -22,7 +22,6 @@ namespace fa {
 namespace {
 
 __device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
 __device__ __forceinline__ float quad_sum(float x) {
   x += __shfl_xor(x, 1);
@@ -224,8 +223,5 @@ hipError_t dispatch(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream) { return dispatch<float>(p, stream); }
-
-// bf16 inputs on the same vector-ALU kernels (widened to fp32 on load).
-hipError_t launch_bwd_bf16_valu(const BwdParams& p, hipStream_t stream) { return dispatch<uint16_t>(p, stream); }
 
 }  // namespace fa

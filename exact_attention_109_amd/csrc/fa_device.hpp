@@ -66,4 +66,74 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+#define LDS_AS __attribute__((address_space(3)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest even) into one register with a single
+// v_cvt_pk_bf16_f32; `lo` lands in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4).
+// The LDS address must be uniform across the wave; lane l writes the 16
+// bytes at ldst + 16*l.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_AS void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+}
+// 4 bytes per lane (lane l writes ldst + 4*l).
+__device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Row of a 32-row MFMA A operand that lane m supplies, chosen so that the
+// 32x32 accumulator register i of lane half g holds row 16*g + i: each lane
+// then owns runs of 8 consecutive rows, the k-layout of a following MFMA
+// whose B operand is taken straight from those accumulators.
+__device__ __forceinline__ int row_of_lane(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// Two ds_read_b64_tr_b16 reads (rows r..r+3 and r+4..r+7 of a row-major bf16
+// tile, addressed per lane as for a transposed 16-bit read) combined into one
+// 8-element MFMA operand: element e = row r+e at this lane's column.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint8_t* p0, const uint8_t* p1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p1));
+  u32x4 v;
+  v[0] = __builtin_bit_cast(u32x2, lo)[0];
+  v[1] = __builtin_bit_cast(u32x2, lo)[1];
+  v[2] = __builtin_bit_cast(u32x2, hi)[0];
+  v[3] = __builtin_bit_cast(u32x2, hi)[1];
+  return as_bf16x8(v);
+}
+
+// Workgroup -> (key/value head index, tile rank). Workgroups are dealt to the
+// 8 XCDs round-robin; when the number of key/value heads allows it, each XCD
+// gets whole key/value heads (all their query heads and tiles) so that K/V
+// is shared through that XCD's L2. Within a head the tile rank runs fastest.
+struct TileAssign {
+  int kvidx, gq, tile_rank;
+};
+__device__ __forceinline__ TileAssign assign_tile(int L, int n_tiles, int G, int xcd_remap) {
+  TileAssign a;
+  if (xcd_remap) {
+    const int xcd = L & 7;
+    const int s = L >> 3;
+    a.tile_rank = s % n_tiles;
+    const int head_local = s / n_tiles;
+    a.kvidx = xcd + 8 * (head_local / G);
+    a.gq = head_local % G;
+  } else {
+    a.tile_rank = L % n_tiles;
+    const int hi = L / n_tiles;
+    a.kvidx = hi / G;
+    a.gq = hi % G;
+  }
+  return a;
+}
+
 }  // namespace fa

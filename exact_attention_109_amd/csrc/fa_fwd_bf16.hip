@@ -52,10 +52,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;       // query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;  // log2 units: skip the rescale while max grows by <= 2^8
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#define LDS_AS __attribute__((address_space(3)))
 
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008;
@@ -92,22 +88,6 @@ __device__ __forceinline__ int swz_v(int row) {
   else return ((row >> 1) & 1) << 2;
 }
 
-// Key held by A-operand row m of a 32-key subtile. With this order the S^T
-// accumulator register i of lane half g holds key 16*g + i, so each lane's
-// probabilities come out as runs of 8 consecutive keys -- the layout of the
-// B operand of the P V contraction.
-__device__ __forceinline__ int key_of_row(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
-
-__device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_AS void* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
@@ -135,24 +115,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int G = H_q / H_kv;
 
   // ---- schedule: workgroup -> (batch, head, query tile)
-  const int L = blockIdx.x;
-  int tile_rank, kvidx, gq;
-  if (xcd_remap) {
-    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD whole
-    // key/value heads (with all their query heads and tiles) so K/V is shared
-    // through that XCD's L2.
-    const int xcd = L & 7;
-    const int s = L >> 3;
-    tile_rank = s % n_qtiles;
-    const int head_local = s / n_qtiles;
-    kvidx = xcd + 8 * (head_local / G);
-    gq = head_local % G;
-  } else {
-    tile_rank = L % n_qtiles;
-    const int hi = L / n_qtiles;
-    kvidx = hi / G;
-    gq = hi % G;
-  }
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap);
+  const int kvidx = ta.kvidx, gq = ta.gq, tile_rank = ta.tile_rank;
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
   const int h = hk * G + gq;
@@ -225,8 +189,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   // ---- per-lane LDS read offsets (bytes within a tile)
-  // K (S^T A operand): row key_of_row(col) of subtile n (n adds 32 rows), chunk (D/16)*half + t.
-  const int krow = key_of_row(col);
+  // K (S^T A operand): row row_of_lane(col) of subtile n (n adds 32 rows), chunk (D/16)*half + t.
+  const int krow = row_of_lane(col);
   int koff[C::QK_STEPS];
 #pragma unroll
   for (int t = 0; t < C::QK_STEPS; ++t)

@@ -29,7 +29,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: D_i = <dO_i, o_i>, [B][H_q][N_q] float32
+  float* delta;  // workspace: D_i = <dO_i, o_i> then lse_i*log2(e), each [B][H_q][N_q] float32
   int B, H_q, H_kv, N_q, N_kv, d;
   int causal;
   float scale;

@@ -90,8 +90,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs for a
  * problem with B batches, H_q query heads and N_q query rows (a multiple of
- * 256). The workspace holds per-row float32 statistics; its content on entry
- * does not matter and on return is unspecified.
+ * 256): two float32 values per query row. Its content on entry does not
+ * matter and on return is unspecified.
  */
 size_t fa_bwd_workspace_size(int B, int H_q, int N_q);
 

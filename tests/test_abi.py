@@ -49,7 +49,7 @@ def test_status_strings(lib):
 
 
 def test_workspace_size():
-    assert fa.fa_bwd_workspace_size(2, 16, 4096) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(2, 16, 4096) == 2 * 2 * 16 * 4096 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 3) == 256
     assert fa.fa_bwd_workspace_size(0, 1, 3) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 65) % 256 == 0

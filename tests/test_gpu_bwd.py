@@ -97,9 +97,10 @@ def test_gqa_config_c4_shape_reduced():
     dq, dk, dv = run_fwd_bwd(inp, True, default_scale(128))
     q, k, v, do = inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do")
     gq, gk, gv = oracle.attention_backward(q[:, :8], k[:, :2], v[:, :2], do[:, :8], True, default_scale(128))
-    assert max_abs(dq[:, :8], gq) <= 1e-2
-    assert max_abs(dk[:, :2], gk) <= 1e-2
-    assert max_abs(dv[:, :2], gv) <= 1e-2
+    errs = (max_abs(dq[:, :8], gq), max_abs(dk[:, :2], gk), max_abs(dv[:, :2], gv))
+    print("GQA max-abs (dq, dk, dv):", errs, "max|ref|:", (np.abs(gq).max(), np.abs(gk).max(), np.abs(gv).max()))
+    for e, ref in zip(errs, (gq, gk, gv)):
+        assert e <= grad_tol(ref, DTYPE_BF16)
 
 
 def test_determinism():
