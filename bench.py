@@ -98,8 +98,13 @@ def time_backward(fa, torch, steps: int, warmup: int):
     q, k, v, do = (inp.torch(n, "cuda") for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     ws = torch.empty((fa.fa_bwd_workspace_size(w.B, w.H_q, w.N_q),), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < 1.0:
         fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     a = torch.cuda.Event(enable_timing=True)
@@ -122,6 +127,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement on c5")
@@ -160,9 +167,18 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
 
-    for _ in range(args.warmup):
+    # W untimed warm-up steps, continued until the GPU has been busy for at
+    # least --warmup-seconds: clocks ramp up under load, and a few
+    # millisecond-long launches would otherwise be timed at idle clocks.
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_warm
 
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
@@ -194,6 +210,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
