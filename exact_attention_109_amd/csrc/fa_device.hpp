@@ -84,12 +84,45 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 __device__ __forceinline__ void lds_dma16(const void* gsrc, LDS_AS void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
+// The same 16-byte LDS DMA from a wave-uniform global base plus a per-lane
+// 32-bit byte offset (the SGPR-base addressing form, so no 64-bit per-lane
+// address is ever formed), issued through inline assembly. The compiler does
+// not track it and inserts no wait for it: the issuing wave must wait_vmem()
+// before any wave reads the data. `lds_addr` is the wave-uniform LDS byte
+// address of the 1 KiB destination (lane l writes lds_addr + 16*l). M0 is
+// written here; nothing else in these kernels uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)(p)));
+}
+
 // 4 bytes per lane (lane l writes ldst + 4*l).
 __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 4, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Workgroup barrier without a memory fence. __syncthreads() also waits for
+// every outstanding memory operation of the wave (s_waitcnt vmcnt(0)
+// lgkmcnt(0) before s_barrier), which would stall a wave that has just
+// issued LDS-DMA prefetches for their whole global-memory latency. Here the
+// caller orders memory itself: LDS data a wave read before the barrier has
+// been consumed by then (its reads are complete), and LDS-DMA writes are
+// waited for with wait_vmem() by the issuing wave before the barrier that
+// publishes them. The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Row of a 32-row MFMA A operand that lane m supplies, chosen so that the
 // 32x32 accumulator register i of lane half g holds row 16*g + i: each lane

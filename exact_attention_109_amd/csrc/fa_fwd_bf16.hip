@@ -28,8 +28,12 @@
 //    one wave of each SIMD drives the matrix core while its partner runs the
 //    softmax on the vector ALU.
 //  * K and V blocks stream from HBM straight into LDS with 16-byte
-//    global_load_lds_dwordx4 issued by group B during its vector phase
-//    (no register staging, double-buffered). Tiles are row-major with
+//    global_load_lds_dwordx4 (no register staging, double-buffered), issued
+//    by group B one at a time between the exponentials of its vector phase:
+//    a wave stalls at a vector-memory instruction until the CU's load path
+//    accepts it, so a burst would cost the whole transfer time. The phase
+//    barriers carry no memory fence, so the loads stay in flight across the
+//    next phase and are waited for only before the barrier that publishes them. Tiles are row-major with
 //    XOR-swizzled 16-byte chunks chosen so that every LDS read is free of bank
 //    conflicts. The V^T operand is read with ds_read_b64_tr_b16, which
 //    transposes 16-bit elements across lanes.
@@ -37,9 +41,10 @@
 //    and exponentiated with v_exp_f32; LSE is converted back with ln 2. The
 //    output rescale is skipped unless some row's max grew by more than 2^8
 //    (exact: the final division and the LSE use the same, possibly stale, max).
-//  * Causal: K/V blocks past the tile's last row are never loaded; waves whose
-//    rows all precede a block skip its work; masking runs only on blocks that
-//    cross the diagonal or the end of the keys.
+//  * Causal: K/V blocks past the tile's last row are never loaded; masking
+//    runs only on blocks that cross a wave's diagonal or the end of the keys.
+
+#include <type_traits>
 
 #include "fa_device.hpp"
 #include "fa_internal.h"
@@ -54,7 +59,9 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: skip the rescale while max
 
 
 // sched_group_barrier instruction classes
+constexpr int kSgValu = 0x402;   // VALU (non-MFMA) and transcendental
 constexpr int kSgMfma = 0x008;
+constexpr int kSgVmem = 0x010;
 constexpr int kSgDsRead = 0x100;
 
 template <int D>
@@ -138,16 +145,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int t = 0; t < C::QK_STEPS; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
   }
 
-  // ---- blocks visited by the workgroup (nblk) and computed by this wave (nact)
+  // ---- key blocks visited by the workgroup. Every wave computes all of them:
+  // the phase barriers make a block cost the same time whether or not a wave
+  // skips it, and a block entirely past a wave's rows is masked to exact
+  // zeros (every row sees key 0 in block 0, so its running max is finite
+  // from then on and exp2 of a masked score is 0).
   const int nblk_all = (N_kv + BC - 1) / BC;
   int nblk = nblk_all;
   if (CAUSAL) {
     const int last_row = min(q0 + kBR, N_q) - 1;
     nblk = min(nblk_all, last_row / BC + 1);
   }
-  const int wlast = min(wrow0 + 31, N_q - 1);
-  int nact = 0;
-  if (wrow0 < N_q) nact = CAUSAL ? min(nblk, wlast / BC + 1) : nblk;
   auto need_mask = [&](int j) __attribute__((always_inline)) {
     const int kv0 = j * BC;
     return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
@@ -157,35 +165,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // KiB of a tile. Instruction i writes bytes [1024*ig, 1024*ig + 1024) of the
   // tile, lane l the 16 bytes at 16*l: row RPI*ig + l/CPR, physical chunk
   // l%CPR, which holds logical chunk (l%CPR) ^ swz(row).
-  uint32_t dma_koff[C::DMA_PER_WAVE];
-  uint32_t dma_voff[C::DMA_PER_WAVE];
+  // The *_t offsets serve the last key block when N_kv is not a multiple of
+  // BC: they read row min(row, last valid row) instead (finite data for the
+  // masked keys, and no access past the end of K and V).
+  const int tail_blk = (N_kv % BC) ? N_kv / BC : -1;
+  const int tail_lim = N_kv - 1 - (N_kv / BC) * BC;
+  uint32_t dma_koff[C::DMA_PER_WAVE], dma_voff[C::DMA_PER_WAVE];
+  uint32_t dma_koff_t[C::DMA_PER_WAVE], dma_voff_t[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
     const int ig = gw * C::DMA_PER_WAVE + i;
     const int row = C::RPI * ig + lane / C::CPR;
     const int p = lane % C::CPR;
+    const int cut = (row - min(row, tail_lim)) * C::ROW_BYTES;
     dma_koff[i] = row * C::ROW_BYTES + (p ^ swz_k<D>(row)) * 16;
     dma_voff[i] = row * C::ROW_BYTES + (p ^ swz_v<D>(row)) * 16;
+    dma_koff_t[i] = dma_koff[i] - cut;
+    dma_voff_t[i] = dma_voff[i] - cut;
   }
-  // One tile (K or V) of block j into LDS. Full blocks address from a uniform
-  // base plus a per-lane 32-bit offset; the last block clamps rows to N_kv-1.
-  auto dma_tile = [&](int j, const uint8_t* src, const uint32_t (&off)[C::DMA_PER_WAVE], uint8_t* dst)
+  // DMA slot i of a vector phase of group B: slots 0 .. DMA_PER_WAVE-1 stage
+  // 1 KiB pieces of the K tile at key block jk, the others pieces of the V
+  // tile at block jv, each from a uniform base plus a per-lane 32-bit offset
+  // (the clamped one for block tail_blk, picked by a uniform select).
+  auto dma_slot = [&](int i, int jk, int jv, uint8_t* kdst, uint8_t* vdst)
       __attribute__((always_inline)) {
-    const int kv0 = j * BC;
-    if (kv0 + BC <= N_kv) {
-      const uint8_t* base = src + size_t(kv0) * C::ROW_BYTES;
+    const bool is_k = i < C::DMA_PER_WAVE;
+    const int ii = is_k ? i : i - C::DMA_PER_WAVE;
+    const int jb = is_k ? jk : jv;
+    const uint8_t* src = (is_k ? Kbytes : Vbytes) + size_t(jb) * BC * C::ROW_BYTES;
+    uint32_t off = is_k ? dma_koff[ii] : dma_voff[ii];
+    if (jb == tail_blk) off = is_k ? dma_koff_t[ii] : dma_voff_t[ii];
+    lds_dma16_sbase(src, off, lds_address(is_k ? kdst : vdst) + 1024 * (gw * C::DMA_PER_WAVE + ii));
+  };
+  // K_0 for the prologue (only group B calls it)
+  auto dma_k0 = [&](uint8_t* kdst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < C::DMA_PER_WAVE; ++i)
-        lds_dma16(base + off[i], (LDS_AS void*)(dst + 1024 * (gw * C::DMA_PER_WAVE + i)));
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-        const int row = int(off[i] / C::ROW_BYTES);
-        const int grow = min(kv0 + row, N_kv - 1);
-        lds_dma16(src + size_t(grow) * C::ROW_BYTES + (off[i] % C::ROW_BYTES),
-                  (LDS_AS void*)(dst + 1024 * (gw * C::DMA_PER_WAVE + i)));
-      }
-    }
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_slot(i, 0, 0, kdst, kdst);
   };
 
   // ---- per-lane LDS read offsets (bytes within a tile)
@@ -269,8 +284,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
   auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-    const bool do_pv = j >= 1 && j - 1 < nact;
-    const bool do_qk = j < nact;
+    const bool do_pv = j >= 1;
+    const bool do_qk = j < nblk;
     if (do_pv) {
       pv_part(vt);
       pv_schedule();
@@ -284,9 +299,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   // Vector phase for block j: mask, block max, (rare) rescale, exponentials,
-  // row sums and bf16 packing.
-  auto valu_phase = [&](int j) __attribute__((always_inline)) {
-    if (j < 0 || j >= nact) return;
+  // row sums and bf16 packing. `issue(i)`, i = 0 .. kDmaSlots-1, issues the
+  // LDS-DMA instructions of the loading group; they are spread through the
+  // exponential loop (a wave that issues a vector-memory instruction stalls
+  // until the CU's load pipeline accepts it, so a burst of them would stall
+  // the wave for the whole transfer instead of overlapping it).
+  constexpr int kDmaSlots = 2 * C::DMA_PER_WAVE;
+  constexpr int kSlotsPerStep = kDmaSlots / C::PV_STEPS;
+  static_assert(kSlotsPerStep * C::PV_STEPS == kDmaSlots, "DMA slots per exponential step");
+  auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
+    constexpr bool kDma = decltype(has_dma)::value;
+    if constexpr (!kDma) {
+      if (j >= nblk) return;  // the step that only finishes PV of the last block
+    }
     if (need_mask(j)) {
       const int kv0 = j * BC;
 #pragma unroll
@@ -326,36 +351,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+      if constexpr (kDma) {
+#pragma unroll
+        for (int r = 0; r < kSlotsPerStep; ++r) issue(u * kSlotsPerStep + r);
+      }
+    }
+    if constexpr (kDma) {
+      // about 28 vector instructions per exponential step (8 x fma, exp,
+      // add; 4 x pack), split evenly between the DMA slots of the step
+#pragma unroll
+      for (int i = 0; i < kDmaSlots; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 28 / kSlotsPerStep, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
     }
     l_run += psum;
   };
 
   // Two phases (ticks) per block j. Group A: MFMA(j) | VALU(j).
   // Group B: VALU(j-1) + DMA of K_{j+1}, V_j | MFMA(j), then wait for the DMA.
+  // The phase barriers carry no memory fence: every LDS read of a phase is
+  // consumed by an MFMA of the same phase, so a buffer is free for the next
+  // DMA once the barrier after its last reading phase has passed, and DMA
+  // data is waited for explicitly one phase after it was issued.
   // Buffers: K_j in kb[j%2], V_j in vb[j%2]. Each group runs its own loop
   // (the group test is outside the loop, so the compiler never has to keep
   // both groups' register state alive across the barriers); both loops pass
   // the same 2*(nblk+1) barriers.
+  auto no_dma = [](int) __attribute__((always_inline)) {};
   auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
     mfma_phase(j, k_cur, v_prev);
-    __syncthreads();
-    valu_phase(j);
-    __syncthreads();
+    barrier_nofence();
+    valu_phase(j, no_dma, std::false_type{});
+    barrier_nofence();
   };
   auto block_b = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev, uint8_t* k_dma, uint8_t* v_dma)
       __attribute__((always_inline)) {
-    valu_phase(j - 1);
-    if (j + 1 < nblk) dma_tile(j + 1, Kbytes, dma_koff, k_dma);
-    if (j < nblk) dma_tile(j, Vbytes, dma_voff, v_dma);
-    __syncthreads();
+    // K_{j+1} and V_j; past the last block the last one is loaded again into
+    // a buffer nobody reads any more, which keeps the issue slots unconditional.
+    const int jk = min(j + 1, nblk - 1);
+    const int jv = min(j, nblk - 1);
+    valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
+      dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
+    barrier_nofence();  // the DMA stays in flight through the next phase
     mfma_phase(j, k_cur, v_prev);
-    wait_vmem();
-    __syncthreads();
+    wait_vmem();        // K_{j+1} and V_j are in LDS before the barrier publishes them
+    barrier_nofence();
   };
 
   // ---- prologue: K_0 into kb0
   if (grp == 1) {
-    dma_tile(0, Kbytes, dma_koff, kb0);
+    dma_k0(kb0);
     wait_vmem();
   }
   __syncthreads();
@@ -367,9 +413,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (j + 1 <= nblk) block_a(j + 1, kb1, vb0);
     }
   } else {
-    for (int j = 0; j <= nblk; j += 2) {
-      block_b(j, kb0, vb1, kb1, vb0);
-      if (j + 1 <= nblk) block_b(j + 1, kb1, vb0, kb0, vb1);
+    // Step 0 has no softmax yet: only the loads of K_1 and V_0, then QK^T of
+    // block 0 (peeled, so that every vector phase in the loop has work).
+    {
+      const int jk = min(1, nblk - 1);
+#pragma unroll
+      for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, 0, kb1, vb0);
+      barrier_nofence();
+      mfma_phase(0, kb0, vb1);
+      wait_vmem();
+      barrier_nofence();
+    }
+    for (int j = 1; j <= nblk; j += 2) {
+      block_b(j, kb1, vb0, kb0, vb1);
+      if (j + 1 <= nblk) block_b(j + 1, kb0, vb1, kb1, vb0);
     }
   }
 
