@@ -313,14 +313,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (j >= nblk) return;  // the step that only finishes PV of the last block
     }
     if (need_mask(j)) {
-      const int kv0 = j * BC;
+      // key kv0 + 32n + 16*half + i is visible iff it is <= last_key (the
+      // row itself when causal, and < N_kv); one compare against the
+      // register's constant key offset per score.
+      const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
+      const int lim = last_key - j * BC - 16 * half;
 #pragma unroll
       for (int n = 0; n < NSUB; ++n)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * n + 16 * half + i;
-          if ((CAUSAL && key > qrow) || key >= N_kv) sacc[n][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * n + i > lim) sacc[n][i] = -INFINITY;
     }
     float mx = sacc[0][0];
 #pragma unroll
