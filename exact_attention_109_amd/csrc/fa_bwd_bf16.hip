@@ -21,11 +21,17 @@
 //  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
 //          owns 32 queries (Q and dO as register operands) while the K/V
 //          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
-//          dQ^T += K^T dS^T with K read transposed.
+//          dQ^T += K^T dS^T with K read transposed. Software-pipelined: the
+//          vector work of block j is issued together with the MFMAs of block
+//          j+1 (S and dP double-buffered), and K/V arrive by LDS-DMA two
+//          blocks ahead through fence-free barriers.
 // The accumulator layouts are arranged so that P and dS leave the MFMA
 // accumulators already in the k-layout of the next contraction's B operand
 // (see row_of_lane), and every LDS tile uses one XOR swizzle that is free of
 // bank conflicts for both its row reads and its transposed reads.
+
+#include <climits>
+#include <type_traits>
 
 #include "fa_device.hpp"
 #include "fa_internal.h"
@@ -44,14 +50,14 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1);
 }
 
-template <int D>
+template <int D, int BLOCK = 64>
 struct BwdCfg {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;       // rows per 1 KiB LDS-DMA instruction
   static constexpr int KST = D / 16;         // MFMA k-steps over the head dimension
   static constexpr int DSUB = D / 32;        // 32-column output subtiles
-  static constexpr int BLK = 64;             // rows (queries or keys) per streamed block
+  static constexpr int BLK = BLOCK;          // rows (queries or keys) per streamed block: 32 or 64
   static constexpr int NSUB = BLK / 32;      // 32-row subtiles of a block
   static constexpr int STEPS = BLK / 16;     // MFMA k-steps over a block
   static constexpr int TILE_BYTES = BLK * D * 2;
@@ -149,6 +155,26 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Shared pieces of the two main kernels
+// ---------------------------------------------------------------------------
+constexpr int kNBuf = 4;  // LDS buffers of streamed blocks: two in use, two loading
+
+// sched_group_barrier instruction classes
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+
+// MFMA-phase schedule: `ahead` LDS reads first, then one read behind each
+// MFMA (so each operand arrives several MFMAs before it is used).
+template <int NMFMA, int READS_PER_MFMA, int AHEAD>
+__device__ __forceinline__ void schedule_mfma_reads() {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, READS_PER_MFMA, 0);
+  }
+}
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
@@ -345,6 +371,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // ---------------------------------------------------------------------------
 constexpr int kQueriesPerWg = 128;  // 4 waves x 32 queries
 
+// Per wave (32 queries) and streamed key block j (64 keys):
+//   X(j): S^T = K Q^T, dP^T = V dO^T          (MFMA, K/V rows from LDS)
+//   Y(j): P, dS^T = P (dP - D), packed         (VALU)
+//   Z(j): dQ^T += K^T dS^T                     (MFMA, K read transposed)
+// Iteration j runs Y(j) interleaved with X(j+1) (S/dP double-buffered), then
+// Z(j); the LDS-DMA of block j+3 is issued between the vector work (two
+// blocks of lookahead beyond the one X reads).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -353,10 +386,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     float scale) {
   using C = BwdCfg<D>;
   constexpr int BK = C::BLK;
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[C::TILE_BYTES];
+  constexpr int DPW = C::DMA_PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[kNBuf][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[kNBuf][C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -388,65 +420,108 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   const float l2 = L2[rbase + qc];
   const float dl = Dl[rbase + qc];
+  wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
 
+  // key blocks of the workgroup; every wave runs all of them (blocks past a
+  // wave's queries are masked to zero).
   const int nblk_all = (N_kv + BK - 1) / BK;
   int nblk = nblk_all;
   if (CAUSAL) nblk = min(nblk_all, (min(q0 + kQueriesPerWg, N_q) - 1) / BK + 1);
-  const int wlast = min(wq0 + 31, N_q - 1);
-  int nact = 0;
-  if (wq0 < N_q) nact = CAUSAL ? min(nblk, wlast / BK + 1) : nblk;
 
-  uint32_t dma_off[C::DMA_PER_WAVE];
-  dma_offsets<D>(wave, lane, dma_off);
-  ReadOffsets<D> ro;
-  ro.init(lane);
+  const int tail_blk = (N_kv % BK) ? N_kv / BK : -1;
+  const int tail_lim = (N_kv - 1) % BK;
+  uint32_t doff[DPW], doff_t[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int ig = wave * DPW + i;
+    const int row = C::RPI * ig + lane / C::CPR;
+    const int pch = lane % C::CPR;
+    doff[i] = row * C::ROW_BYTES + (pch ^ swz<D>(row)) * 16;
+    doff_t[i] = doff[i] - (row - min(row, tail_lim)) * C::ROW_BYTES;
+  }
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + kvbase);
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + kvbase);
+  constexpr int kSlots = 2 * DPW;
+  auto dma_slot = [&](int i, int j, int bf) __attribute__((always_inline)) {
+    const bool is_k = i < DPW;
+    const int ii = is_k ? i : i - DPW;
+    const uint8_t* src = (is_k ? Kb : Vb) + size_t(j) * BK * C::ROW_BYTES;
+    lds_dma16_sbase_nc(src, j == tail_blk ? doff_t[ii] : doff[ii],
+                       lds_address(is_k ? ks[bf] : vs[bf]) + 1024 * (wave * DPW + ii));
+  };
+
+  ReadOffsets<D> ro;
+  ro.init(lane);
 
   f32x16 dq[C::DSUB];
 #pragma unroll
   for (int s = 0; s < C::DSUB; ++s) dq[s] = f32x16{};
+  f32x16 sA[C::NSUB], pA[C::NSUB], sB[C::NSUB], pB[C::NSUB];  // S^T, dP^T of two blocks
+  u32x4 sk[C::STEPS];                                          // dS^T (bf16) of the current block
 
-  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-    if (j >= nact) return;
-    const int kv0 = j * BK;
-    // S^T = K Q^T, dP^T = V dO^T (keys x queries; lane = query, register i of
-    // subtile n = key 32n + 16*half + i)
-    f32x16 sacc[C::NSUB], pacc[C::NSUB];
+  constexpr int NX = 2 * C::KST * C::NSUB;  // MFMAs of X
+  constexpr int NZ = C::STEPS * C::DSUB;    // MFMAs of Z
+  // X(j) from buffer bf into (s, p)
+  auto X = [&](int bf, f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
+    const uint8_t* kt = ks[bf];
+    const uint8_t* vt = vs[bf];
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
-      sacc[n] = f32x16{};
-      pacc[n] = f32x16{};
+      sx[n] = f32x16{};
+      px[n] = f32x16{};
     }
 #pragma unroll
     for (int t = 0; t < C::KST; ++t) {
 #pragma unroll
       for (int n = 0; n < C::NSUB; ++n) {
         const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
-        sacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o)), qreg[t], sacc[n]);
-        pacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vt + o)), oreg[t], pacc[n]);
+        sx[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o)), qreg[t], sx[n]);
+        px[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vt + o)), oreg[t], px[n]);
       }
     }
-    const bool need_mask = (CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv);
-    u32x4 sk[C::STEPS];
+  };
+  // Scores of block j past this lane's query (causal) or past N_kv become
+  // -inf, so that P and dS are exactly 0 there.
+  auto mask_scores = [&](int j, f32x16 (&s)[C::NSUB]) __attribute__((always_inline)) {
+    // key j*BK + 32n + 16*half + i is visible iff 32n + i <= lim
+    const int last_key = CAUSAL ? min(query, N_kv - 1) : N_kv - 1;
+    const int lim = last_key - j * BK - 16 * half;
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * n + i > lim) s[n][i] = -INFINITY;
+  };
+  // Y(j) on (s, p) -> sk; with WITH_X also X(j+1) from buffer bfx into
+  // (sx, px) and the DMA of block jd into buffer bfd.
+  auto YX = [&](auto with_x, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], int bfx,
+                f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB], int jd, int bfd) __attribute__((always_inline)) {
+    constexpr bool WITH_X = decltype(with_x)::value;
+    if constexpr (WITH_X) X(bfx, sx, px);
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[n][i], c, -l2));
-        if (need_mask) {
-          const int kk = kv0 + 32 * n + 16 * half + i;
-          if ((CAUSAL && kk > query) || kk >= N_kv) p = 0.f;
+        const float pv = fast_exp2(fmaf(s[n][i], c, -l2));
+        p[n][i] = pv * (p[n][i] - dl);
+        if constexpr (WITH_X) {
+          const int e = 16 * n + i;
+          if (e % 3 == 1 && e / 3 < kSlots) dma_slot(e / 3, jd, bfd);
         }
-        pacc[n][i] = p * (pacc[n][i] - dl);
       }
 #pragma unroll
       for (int w = 0; w < 2; ++w)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sk[2 * n + w][e] = cvt_pk_bf16(pacc[n][8 * w + 2 * e], pacc[n][8 * w + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(p[n][8 * w + 2 * e], p[n][8 * w + 2 * e + 1]);
     }
-    // dQ^T += K^T dS^T (d x queries; K read transposed)
+    if constexpr (WITH_X) {
+#pragma unroll
+      for (int e = 32 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
+      // about 4.5 vector instructions per element over the MFMAs of X(j+1)
+    }
+  };
+  auto Z = [&](int bf) __attribute__((always_inline)) {
+    const uint8_t* kt = ks[bf];
 #pragma unroll
     for (int u = 0; u < C::STEPS; ++u) {
       const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
@@ -456,29 +531,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         dq[s] = mfma32x32x16(a, as_bf16x8(sk[u]), dq[s]);
       }
     }
+    schedule_mfma_reads<NZ - 4, 2, 8>();
+  };
+  auto need_mask = [&](int j) __attribute__((always_inline)) {
+    const int kv0 = j * BK;
+    return (CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv);
+  };
+  // iteration j (< nblk - 1): Y(j) on (s, p) with X(j+1) into (sx, px), then Z(j)
+  auto iteration = [&](int j, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], f32x16 (&sx)[C::NSUB],
+                       f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
+    const int jd = min(j + 3, nblk - 1);  // past the end: a harmless reload into a free buffer
+    if (need_mask(j)) mask_scores(j, s);
+    __builtin_amdgcn_sched_barrier(0);
+    YX(std::true_type{}, s, p, (j + 1) % kNBuf, sx, px, jd, (j + 3) % kNBuf);
+    __builtin_amdgcn_sched_barrier(0);
+    Z(j % kNBuf);
+    wait_vmem_keep<kSlots>();  // block j+2 (loaded since the last iteration) is in LDS
+    barrier_nofence();
+  };
+  auto last = [&](int j, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB]) __attribute__((always_inline)) {
+    if (need_mask(j)) mask_scores(j, s);
+    __builtin_amdgcn_sched_barrier(0);
+    YX(std::false_type{}, s, p, 0, sB, pB, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    Z(j % kNBuf);
   };
 
-  dma_tile<D>(Kb, 0, N_kv, dma_off, ks0, wave);
-  dma_tile<D>(Vb, 0, N_kv, dma_off, vs0, wave);
+  // blocks 0, 1, 2 into buffers 0, 1, 2, X(0), then the pipeline
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) dma_slot(i, min(1, nblk - 1), 1);
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) dma_slot(i, min(2, nblk - 1), 2);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < nblk; j += 2) {
-    if (j + 1 < nblk) {
-      dma_tile<D>(Kb, (j + 1) * BK, N_kv, dma_off, ks1, wave);
-      dma_tile<D>(Vb, (j + 1) * BK, N_kv, dma_off, vs1, wave);
-    }
-    compute(j, ks0, vs0);
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < nblk) {
-      if (j + 2 < nblk) {
-        dma_tile<D>(Kb, (j + 2) * BK, N_kv, dma_off, ks0, wave);
-        dma_tile<D>(Vb, (j + 2) * BK, N_kv, dma_off, vs0, wave);
-      }
-      compute(j + 1, ks1, vs1);
-      wait_vmem();
-      __syncthreads();
-    }
+  X(0, sA, pA);
+  schedule_mfma_reads<NX - 4, 1, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  int j = 0;
+  for (; j + 2 < nblk; j += 2) {
+    iteration(j, sA, pA, sB, pB);
+    iteration(j + 1, sB, pB, sA, pA);
+  }
+  if (j + 1 < nblk) {
+    iteration(j, sA, pA, sB, pB);
+    last(j + 1, sB, pB);
+  } else {
+    last(j, sA, pA);
   }
 
   if (query < N_q) {

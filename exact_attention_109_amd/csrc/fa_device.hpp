@@ -97,6 +97,17 @@ __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                : : "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+// Variants without the compiler memory clobber, for code that interleaves
+// the DMA with LDS reads of other buffers: the compiler may move loads across
+// them. They stay ordered with respect to barrier_nofence() and the waits
+// (volatile asm and side-effecting builtins are not reordered), which is what
+// protects the destination buffer. The 4-byte form writes lds_addr + 4*l.
+__device__ __forceinline__ void lds_dma16_sbase_nc(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr) : "m0");
+}
+__device__ __forceinline__ void lds_dma4_sbase_nc(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr) : "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS const void*)(p)));
@@ -108,6 +119,13 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (loads complete in order, so everything issued before the last N is done).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // Workgroup barrier without a memory fence. __syncthreads() also waits for
 // every outstanding memory operation of the wave (s_waitcnt vmcnt(0)
