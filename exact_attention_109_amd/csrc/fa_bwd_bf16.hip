@@ -222,6 +222,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       kreg[t] = as_bf16x8(ld_global16(K + off + 8 * t));
       vreg[t] = as_bf16x8(ld_global16(V + off + 8 * t));
     }
+    // The operands are only ever read by MFMAs, which take them from AGPRs:
+    // placing them there leaves the VGPRs to the vector work.
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) asm volatile("" : "+a"(kreg[t]), "+a"(vreg[t]));
   }
 
   // query blocks: for each of the G query heads, blocks from qstart to N_q
@@ -417,6 +421,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       qreg[t] = as_bf16x8(ld_global16(Q + off + 8 * t));
       oreg[t] = as_bf16x8(ld_global16(dO + off + 8 * t));
     }
+    // only MFMAs read these: keep them in AGPRs, out of the vector work's way
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) asm volatile("" : "+a"(qreg[t]), "+a"(oreg[t]));
   }
   const float l2 = L2[rbase + qc];
   const float dl = Dl[rbase + qc];
