@@ -17,7 +17,8 @@
 //          group stream past through LDS. Per 64-query block and wave:
 //          S = Q K^T and dP = dO V^T (queries x keys, Q/dO rows read from LDS),
 //          P and dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
-//          dO/Q operands read transposed (ds_read_b64_tr_b16).
+//          dO/Q operands read transposed (ds_read_b64_tr_b16). Software-
+//          pipelined like dq below.
 //  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
 //          owns 32 queries (Q and dO as register operands) while the K/V
 //          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
@@ -63,42 +64,6 @@ struct BwdCfg {
   static constexpr int TILE_BYTES = BLK * D * 2;
   static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;
 };
-
-// Per-lane byte offsets of the LDS-DMA writes of one tile (this wave's
-// share): row RPI*ig + l/CPR, physical chunk l%CPR = logical chunk ^ swz(row).
-template <int D>
-__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[BwdCfg<D>::DMA_PER_WAVE]) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int ig = wave * C::DMA_PER_WAVE + i;
-    const int row = C::RPI * ig + lane / C::CPR;
-    const int p = lane % C::CPR;
-    off[i] = row * C::ROW_BYTES + (p ^ swz<D>(row)) * 16;
-  }
-}
-
-// Rows [r0, r0 + BLK) of a row-major [rows][D] bf16 matrix into an LDS tile;
-// rows past `nrows` repeat the last row (their results are masked).
-template <int D>
-__device__ __forceinline__ void dma_tile(const uint8_t* src, int r0, int nrows,
-                                         const uint32_t (&off)[BwdCfg<D>::DMA_PER_WAVE], uint8_t* dst, int wave) {
-  using C = BwdCfg<D>;
-  if (r0 + C::BLK <= nrows) {
-    const uint8_t* base = src + size_t(r0) * C::ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i)
-      lds_dma16(base + off[i], (LDS_AS void*)(dst + 1024 * (wave * C::DMA_PER_WAVE + i)));
-  } else {
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const int row = int(off[i] / C::ROW_BYTES);
-      const int grow = min(r0 + row, nrows - 1);
-      lds_dma16(src + size_t(grow) * C::ROW_BYTES + (off[i] % C::ROW_BYTES),
-                (LDS_AS void*)(dst + 1024 * (wave * C::DMA_PER_WAVE + i)));
-    }
-  }
-}
 
 // Per-lane offsets for the row reads (A operand with rows row_of_lane(col),
 // chunk (D/16)*half + t; subtile n adds 32 rows) and the transposed reads
@@ -180,6 +145,13 @@ __device__ __forceinline__ void schedule_mfma_reads() {
 // ---------------------------------------------------------------------------
 constexpr int kKeysPerWg = 128;  // 4 waves x 32 keys
 
+// Per wave (32 keys, K and V as register operands) and streamed query block
+// jb (64 queries of one query head):
+//   X(jb): S = Q K^T, dP = dO V^T                      (MFMA, Q/dO rows from LDS)
+//   Y(jb): P = exp2(S c - L2), dS = P (dP - D), packed  (VALU)
+//   Z(jb): dV^T += dO^T P, dK^T += Q^T dS               (MFMA, Q/dO read transposed)
+// Iteration jb runs Y(jb) interleaved with X(jb+1) (S/dP double-buffered),
+// then Z(jb); the LDS-DMA of block jb+3 is issued between the vector work.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -188,14 +160,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     int xcd_remap, float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int BQ = C::BLK;
-  __shared__ __attribute__((aligned(1024))) uint8_t qs0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t qs1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t os0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t os1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) float ls0[BQ];
-  __shared__ __attribute__((aligned(256))) float ls1[BQ];
-  __shared__ __attribute__((aligned(256))) float ds0[BQ];
-  __shared__ __attribute__((aligned(256))) float ds1[BQ];
+  constexpr int DPW = C::DMA_PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) uint8_t qs[kNBuf][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t os[kNBuf][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float vecs[kNBuf][2][BQ];  // [buffer][L2, D][query]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,37 +190,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       kreg[t] = as_bf16x8(ld_global16(K + off + 8 * t));
       vreg[t] = as_bf16x8(ld_global16(V + off + 8 * t));
     }
-    // The operands are only ever read by MFMAs, which take them from AGPRs:
-    // placing them there leaves the VGPRs to the vector work.
+    // only MFMAs read these: keep them in AGPRs, out of the vector work's way
 #pragma unroll
     for (int t = 0; t < C::KST; ++t) asm volatile("" : "+a"(kreg[t]), "+a"(vreg[t]));
   }
+  wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
 
-  // query blocks: for each of the G query heads, blocks from qstart to N_q
+  // query blocks: for each of the G query heads, blocks from qstart to N_q.
+  // Every wave runs every block of the workgroup (blocks before a wave's keys
+  // are masked to zero).
   const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
   const int nqb = qstart < N_q ? (N_q - qstart + BQ - 1) / BQ : 0;
   const int nblk = G * nqb;
 
-  uint32_t dma_off[C::DMA_PER_WAVE];
-  dma_offsets<D>(wave, lane, dma_off);
-  ReadOffsets<D> ro;
-  ro.init(lane);
+  // LDS-DMA of a block: per-lane offsets within a tile, and clamped ones for
+  // the partial last block of a head (rows past N_q repeat row N_q - 1).
+  const int tail_q0 = (N_q % BQ) ? N_q - N_q % BQ : -1;
+  const int tail_lim = (N_q - 1) % BQ;
+  uint32_t doff[DPW], doff_t[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int ig = wave * DPW + i;
+    const int row = C::RPI * ig + lane / C::CPR;
+    const int pch = lane % C::CPR;
+    doff[i] = row * C::ROW_BYTES + (pch ^ swz<D>(row)) * 16;
+    doff_t[i] = doff[i] - (row - min(row, tail_lim)) * C::ROW_BYTES;
+  }
+  const uint32_t voff = lane * 4, voff_t = min(lane, tail_lim) * 4;
+  const float* vsrc = (wave & 1) ? Dl : L2;  // waves 0, 2: L2; waves 1, 3: D (same bytes twice)
 
   auto block_head = [&](int jb, int& h, int& qb0) __attribute__((always_inline)) {
     const int g = jb / nqb;
     h = hk * G + g;
     qb0 = qstart + (jb % nqb) * BQ;
   };
-  // Q and dO rows of block jb into LDS, plus its L2 and D vectors (64 floats each).
-  auto issue = [&](int jb, uint8_t* qd, uint8_t* od, float* ld, float* dd) __attribute__((always_inline)) {
+  // DMA slot i of block jb into buffer bf: Q pieces, dO pieces, then the vector.
+  constexpr int kSlots = 2 * DPW + 1;
+  auto dma_slot = [&](int i, int jb, int bf) __attribute__((always_inline)) {
     int h, qb0;
     block_head(jb, h, qb0);
     const size_t rbase = (size_t(b) * H_q + h) * size_t(N_q);
-    dma_tile<D>(reinterpret_cast<const uint8_t*>(Q + rbase * D), qb0, N_q, dma_off, qd, wave);
-    dma_tile<D>(reinterpret_cast<const uint8_t*>(dO + rbase * D), qb0, N_q, dma_off, od, wave);
-    if (wave == 0) lds_dma4(L2 + rbase + min(qb0 + lane, N_q - 1), (LDS_AS void*)ld);
-    if (wave == 1) lds_dma4(Dl + rbase + min(qb0 + lane, N_q - 1), (LDS_AS void*)dd);
+    const bool tail = qb0 == tail_q0;
+    if (i < 2 * DPW) {
+      const bool is_q = i < DPW;
+      const int ii = is_q ? i : i - DPW;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>((is_q ? Q : dO) + (rbase + qb0) * D);
+      lds_dma16_sbase_nc(src, tail ? doff_t[ii] : doff[ii],
+                         lds_address(is_q ? qs[bf] : os[bf]) + 1024 * (wave * DPW + ii));
+    } else {
+      lds_dma4_sbase_nc(vsrc + rbase + qb0, tail ? voff_t : voff, lds_address(&vecs[bf][wave & 1][0]));
+    }
   };
+
+  ReadOffsets<D> ro;
+  ro.init(lane);
 
   f32x16 dk[C::DSUB], dv[C::DSUB];
 #pragma unroll
@@ -260,65 +251,86 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     dk[s] = f32x16{};
     dv[s] = f32x16{};
   }
+  f32x16 sA[C::NSUB], pA[C::NSUB], sB[C::NSUB], pB[C::NSUB];  // S, dP of two blocks
+  u32x4 pk[C::STEPS], sk[C::STEPS];                            // P, dS (bf16) of the current block
 
-  auto compute = [&](int jb, const uint8_t* qt, const uint8_t* ot, const float* lt, const float* dt)
-      __attribute__((always_inline)) {
-    int h, qb0;
-    block_head(jb, h, qb0);
-    (void)h;
-    if (CAUSAL && qb0 + BQ - 1 < kw) return;  // every query precedes every key of this wave
-    // S = Q K^T and dP = dO V^T (queries x keys; lane = key, register i of
-    // subtile n = query 32n + 16*half + i)
-    f32x16 sacc[C::NSUB], pacc[C::NSUB];
+  constexpr int NX = 2 * C::KST * C::NSUB;    // MFMAs of X
+  constexpr int NZ = 2 * C::STEPS * C::DSUB;  // MFMAs of Z
+  auto X = [&](int bf, f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
+    const uint8_t* qt = qs[bf];
+    const uint8_t* ot = os[bf];
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
-      sacc[n] = f32x16{};
-      pacc[n] = f32x16{};
+      sx[n] = f32x16{};
+      px[n] = f32x16{};
     }
 #pragma unroll
     for (int t = 0; t < C::KST; ++t) {
 #pragma unroll
       for (int n = 0; n < C::NSUB; ++n) {
         const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
-        sacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o)), kreg[t], sacc[n]);
-        pacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o)), vreg[t], pacc[n]);
+        sx[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o)), kreg[t], sx[n]);
+        px[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o)), vreg[t], px[n]);
       }
     }
-    // P = exp2(S*c - L2_q), dS = P (dP - D_q); masked entries are 0
-    const bool need_mask = (CAUSAL && qb0 < kw + 31) || (qb0 + BQ > N_q);
-    u32x4 pk[C::STEPS], sk[C::STEPS];
+  };
+  // Scores of block jb that no query may attend (query before this lane's
+  // key, or past N_q) become -inf, so that P and dS are exactly 0 there.
+  auto mask_scores = [&](int jb, f32x16 (&sx)[C::NSUB]) __attribute__((always_inline)) {
+    int h, qb0;
+    block_head(jb, h, qb0);
+    (void)h;
+    // query 32n + 16*half + i of the block is visible iff lo <= 32n + i <= hi
+    const int lo = CAUSAL ? key - qb0 - 16 * half : INT_MIN;
+    const int hi = N_q - 1 - qb0 - 16 * half;
+#pragma unroll
+    for (int n = 0; n < C::NSUB; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * n + i < lo || 32 * n + i > hi) sx[n][i] = -INFINITY;
+  };
+  // Y(jb) on (s, p) from buffer bfy -> (pk, sk); with WITH_X also X(jb+1)
+  // from buffer bfx into (sx, px) and the DMA of block jd into buffer bfd.
+  auto YX = [&](auto with_x, int bfy, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], int bfx,
+                f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB], int jd, int bfd) __attribute__((always_inline)) {
+    constexpr bool WITH_X = decltype(with_x)::value;
+    if constexpr (WITH_X) X(bfx, sx, px);
+    const float* lt = vecs[bfy][0];
+    const float* dt = vecs[bfy][1];
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
-      float l2v[16], dlv[16];
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 32 * n + 16 * half + 4 * v4);
         const f32x4 d = *reinterpret_cast<const f32x4*>(dt + 32 * n + 16 * half + 4 * v4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          l2v[4 * v4 + e] = a[e];
-          dlv[4 * v4 + e] = d[e];
+          const int i = 4 * v4 + e;
+          const float pv = fast_exp2(fmaf(s[n][i], c, -a[e]));
+          s[n][i] = pv;
+          p[n][i] = pv * (p[n][i] - d[e]);
+          if constexpr (WITH_X) {
+            const int el = 16 * n + i;
+            if (el % 3 == 1 && el / 3 < kSlots) dma_slot(el / 3, jd, bfd);
+          }
         }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sacc[n][i], c, -l2v[i]));
-        if (need_mask) {
-          const int q = qb0 + 32 * n + 16 * half + i;
-          if ((CAUSAL && key > q) || q >= N_q) p = 0.f;
-        }
-        sacc[n][i] = p;
-        pacc[n][i] = p * (pacc[n][i] - dlv[i]);
       }
 #pragma unroll
       for (int w = 0; w < 2; ++w)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pk[2 * n + w][e] = cvt_pk_bf16(sacc[n][8 * w + 2 * e], sacc[n][8 * w + 2 * e + 1]);
-          sk[2 * n + w][e] = cvt_pk_bf16(pacc[n][8 * w + 2 * e], pacc[n][8 * w + 2 * e + 1]);
+          pk[2 * n + w][e] = cvt_pk_bf16(s[n][8 * w + 2 * e], s[n][8 * w + 2 * e + 1]);
+          sk[2 * n + w][e] = cvt_pk_bf16(p[n][8 * w + 2 * e], p[n][8 * w + 2 * e + 1]);
         }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (d x keys; dO/Q read transposed)
+    if constexpr (WITH_X) {
+#pragma unroll
+      for (int e = 16 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
+    }
+  };
+  auto Z = [&](int bf) __attribute__((always_inline)) {
+    const uint8_t* qt = qs[bf];
+    const uint8_t* ot = os[bf];
 #pragma unroll
     for (int u = 0; u < C::STEPS; ++u) {
       const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
@@ -330,23 +342,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         dk[s] = mfma32x32x16(aq, as_bf16x8(sk[u]), dk[s]);
       }
     }
+    schedule_mfma_reads<NZ - 4, 2, 8>();
+  };
+  auto need_mask = [&](int jb) __attribute__((always_inline)) {
+    int h, qb0;
+    block_head(jb, h, qb0);
+    (void)h;
+    return (CAUSAL && qb0 < kw + 31) || (qb0 + BQ > N_q);
+  };
+  // iteration jb (< nblk - 1): Y(jb) on (s, p) with X(jb+1) into (sx, px), then Z(jb)
+  auto iteration = [&](int jb, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], f32x16 (&sx)[C::NSUB],
+                       f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
+    const int jd = min(jb + 3, nblk - 1);  // past the end: a harmless reload into a free buffer
+    if (need_mask(jb)) mask_scores(jb, s);
+    __builtin_amdgcn_sched_barrier(0);
+    YX(std::true_type{}, jb % kNBuf, s, p, (jb + 1) % kNBuf, sx, px, jd, (jb + 3) % kNBuf);
+    __builtin_amdgcn_sched_barrier(0);
+    Z(jb % kNBuf);
+    wait_vmem_keep<kSlots>();  // block jb+2 (loaded since the last iteration) is in LDS
+    barrier_nofence();
+  };
+  auto last = [&](int jb, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB]) __attribute__((always_inline)) {
+    if (need_mask(jb)) mask_scores(jb, s);
+    __builtin_amdgcn_sched_barrier(0);
+    YX(std::false_type{}, jb % kNBuf, s, p, 0, sB, pB, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    Z(jb % kNBuf);
   };
 
   if (nblk > 0) {
-    issue(0, qs0, os0, ls0, ds0);
+    // blocks 0, 1, 2 into buffers 0, 1, 2, X(0), then the pipeline
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) dma_slot(i, min(1, nblk - 1), 1);
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) dma_slot(i, min(2, nblk - 1), 2);
     wait_vmem();
     __syncthreads();
-  }
-  for (int jb = 0; jb < nblk; jb += 2) {
-    if (jb + 1 < nblk) issue(jb + 1, qs1, os1, ls1, ds1);
-    compute(jb, qs0, os0, ls0, ds0);
-    wait_vmem();
-    __syncthreads();
+    X(0, sA, pA);
+    schedule_mfma_reads<NX - 4, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    int jb = 0;
+    for (; jb + 2 < nblk; jb += 2) {
+      iteration(jb, sA, pA, sB, pB);
+      iteration(jb + 1, sB, pB, sA, pA);
+    }
     if (jb + 1 < nblk) {
-      if (jb + 2 < nblk) issue(jb + 2, qs0, os0, ls0, ds0);
-      compute(jb + 1, qs1, os1, ls1, ds1);
-      wait_vmem();
-      __syncthreads();
+      iteration(jb, sA, pA, sB, pB);
+      last(jb + 1, sB, pB);
+    } else {
+      last(jb, sA, pA);
     }
   }
 
