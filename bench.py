@@ -14,6 +14,7 @@ on a bounded sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -25,7 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import WORKLOADS, make_inputs  # noqa: E402
+from workloads import DECODE_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3
@@ -57,12 +58,28 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def device_clock_khz(torch):
+    """Peak engine clock of device 0 in kHz, from the HIP runtime that torch
+    loaded (hipDeviceGetAttribute with hipDeviceAttributeClockRate = 5)."""
+    try:
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        value = ctypes.c_int(0)
+        if lib.hipDeviceGetAttribute(ctypes.byref(value), 5, 0) == 0 and value.value > 0:
+            return value.value
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, budget_s: float = 12.0):
     """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
     import oracle
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)" for i in info]
     except Exception:
         threads = os.cpu_count() or 1
     G = w.H_q // w.H_kv
@@ -87,6 +104,8 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
         "sample": f"{heads} of {w.B * w.H_q} heads (all {w.N_q} rows each) of {w.name}, fp64 numpy, "
                   f"{el:.1f} s",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "os_cpu_count": os.cpu_count(),
+        "blas": blas,
     }
 
 
@@ -121,6 +140,49 @@ def time_backward(fa, torch, steps: int, warmup: int):
             "note": "FLOP = 2.5 x forward FLOP; the kernels issue 3.5 x (S, dP recomputed in both passes)"}
 
 
+def time_decode(fa, torch, steps: int):
+    """Split-KV forward on the decode workload: HBM-bound, reported as the
+    algorithmic bytes (Q, K, V read once; O, LSE written once) per second
+    against the 8 TB/s HBM peak."""
+    w = DECODE_WORKLOADS["d1"]
+    inp = make_inputs(w)
+    q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = fa.default_num_splits(w.B, w.H_kv, w.N_kv, cus)
+    ws = torch.empty((max(256, fa.fa_fwd_splitkv_workspace_size(w.B, w.H_q, w.N_q, w.d, splits)),),
+                     dtype=torch.uint8, device="cuda")
+    nbytes = (q.numel() + k.numel() + v.numel() + o.numel()) * 2 + lse.numel() * 4
+    t0 = time.perf_counter()
+    n = 0
+    while n < 5 or time.perf_counter() - t0 < 0.5:
+        fa.fwd_splitkv(q, k, v, splits, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+        n += 1
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in per:
+        a.record(stream)
+        fa.fwd_splitkv(q, k, v, splits, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in per]
+    med = float(np.median(ms))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return {
+        "workload": w.name,
+        "entry_point": "fa_fwd_splitkv",
+        "num_splits": splits,
+        "median_ms": round(med, 4),
+        "min_ms": round(float(np.min(ms)), 4),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4)},
+        "tflops": round(w.fwd_flop / (med * 1e-3) / 1e12, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +194,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement on c5")
+    ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
@@ -203,6 +266,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == 1 else PEAK_F32_TFLOPS
 
     props = torch.cuda.get_device_properties(0)
+    clock_khz = device_clock_khz(torch)
     result = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) and fraction of MI355X dense-bf16 MFMA peak",
         "value": round(tflops, 2),
@@ -229,15 +293,24 @@ def main():
             "traffic": measured_traffic(w.name),
             "kernel": "fwd_bf16_kernel" if w.dtype == 1 else "fwd_f32_kernel",
             "avg_launch_ms": round(avg_launch_ms, 4),
+            "median_launch_ms": round(float(np.median(launch_ms)), 4),
+            "min_launch_ms": round(float(np.min(launch_ms)), 4),
             "flop_per_launch": w.fwd_flop,
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""),
+                   "peak_clock_mhz": None if clock_khz is None else clock_khz / 1000,
+                   # dense bf16: 4096 FLOP per clock per CU (32x32x16 MFMA, 4 SIMDs)
+                   "bf16_peak_tflops_from_device": None if clock_khz is None else
+                   round(4096 * props.multi_processor_count * clock_khz * 1e3 / 1e12, 1)},
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_bwd:
         print("# timing the backward on c5", file=sys.stderr, flush=True)
         result["bwd"] = time_backward(fa, torch, max(3, args.steps // 2), 2)
+    if not args.no_decode:
+        print("# timing the split-KV forward on the decode workload", file=sys.stderr, flush=True)
+        result["decode"] = time_decode(fa, torch, max(5, args.steps))
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

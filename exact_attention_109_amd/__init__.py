@@ -1,11 +1,13 @@
 """Exact attention on AMD MI355X (gfx950): Python binding of libfa.so.
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
-fa_bwd_workspace_size and fa_status_string. This module exposes the same
-four names with the same arguments (device pointers as integers, sizes,
-flags, a stream handle) plus two convenience wrappers over torch tensors:
+fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size and
+fa_status_string. This module exposes the same names with the same
+arguments (device pointers as integers, sizes, flags, a stream handle) plus
+convenience wrappers over torch tensors:
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
+    o, lse = fwd_splitkv(q, k, v, num_splits, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
 
 The wrappers only marshal arguments: torch allocates device memory and
@@ -55,6 +57,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -78,6 +84,16 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H_q, 
 
 def fa_bwd_workspace_size(B, H_q, N_q) -> int:
     return load_library().fa_bwd_workspace_size(B, H_q, N_q)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, num_splits, workspace,
+                   workspace_bytes, stream) -> int:
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, int(causal), float(scale),
+                                         dtype, num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits) -> int:
+    return load_library().fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits)
 
 
 def fa_status_string(status: int) -> str:
@@ -138,6 +154,48 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     return out, lse
 
 
+def default_num_splits(B: int, H_kv: int, N_kv: int, num_cus: int) -> int:
+    """Key ranges per (batch, key/value head) for fwd_splitkv: enough
+    workgroups for about two per compute unit, at least 4 tiles of 32 keys
+    (one per wave) in each range, at most 256 ranges."""
+    want = -(-2 * num_cus // max(1, B * H_kv))
+    return int(max(1, min(want, 256, -(-N_kv // 128))))
+
+
+def fwd_splitkv(q, k, v, num_splits: int | None = None, causal: bool = False, scale: float | None = None,
+                out=None, lse=None, workspace=None):
+    """Split-KV forward (bf16; (H_q/H_kv)*N_q <= 32): the same result as fwd,
+    with the keys cut into num_splits ranges that run in parallel (default:
+    default_num_splits for the current device)."""
+    import torch
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    if num_splits is None:
+        num_splits = default_num_splits(B, H_kv, N_kv, torch.cuda.get_device_properties(q.device).multi_processor_count)
+    _check(q, "q")
+    _check(k, "k", q.dtype, (B, H_kv, N_kv, d))
+    _check(v, "v", q.dtype, (B, H_kv, N_kv, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    _check(out, "out", q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    ws_bytes = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H_q, H_kv, N_q, N_kv, d, causal, scale, _dtype_code(q), num_splits, ws_ptr, ws_len,
+                        _stream_handle(q))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_splitkv")
+    return out, lse
+
+
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
     """Attention backward; o and lse from fwd on the same inputs.
 
@@ -167,6 +225,7 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
     return dq, dk, dv
 
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fwd", "bwd", "load_library",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_status_string", "fwd", "fwd_splitkv", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
            "FA_DTYPE_BF16", "LIB_PATH"]

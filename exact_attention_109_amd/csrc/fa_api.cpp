@@ -164,3 +164,54 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   hipError_t err = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, s) : fa::launch_bwd_f32(p, s);
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+FA_EXPORT size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_splits) {
+  if (B <= 0 || H_q <= 0 || N_q <= 0 || d <= 0 || num_splits <= 1) return 0;
+  const size_t bytes = fa::fwd_split_workspace_floats(B, H_q, N_q, d, num_splits) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                             int causal, float scale, int dtype, int num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+
+  const size_t es = elem_size(dtype);
+  const size_t q_bytes = size_t(B) * H_q * N_q * d * es;
+  const size_t kv_bytes = size_t(B) * H_kv * N_kv * d * es;
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  const Range in[3] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(v, kv_bytes)};
+  const Range out[2] = {range_of(o, q_bytes), range_of(lse, lse_bytes)};
+  for (const Range& r : out)
+    for (const Range& i : in)
+      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
+
+  if (num_splits < 1 || num_splits > 256) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if ((H_q / H_kv) * N_q > 32) return FA_ERR_UNSUPPORTED;
+
+  const size_t ws_need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits);
+  if (ws_need > 0) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < ws_need) return FA_ERR_INVALID_ARG;
+    const Range w = range_of(workspace, ws_need);
+    for (const Range& i : in)
+      if (overlaps(w, i)) return FA_ERR_INVALID_ARG;
+    for (const Range& r : out)
+      if (overlaps(w, r)) return FA_ERR_INVALID_ARG;
+  }
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::FwdParams p{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipError_t err = fa::launch_fwd_split_bf16(p, num_splits, static_cast<float*>(workspace),
+                                             reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

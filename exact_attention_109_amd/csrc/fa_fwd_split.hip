@@ -1,0 +1,346 @@
+// Split-KV attention forward for few queries against many keys (decode-like
+// shapes: a handful of new query rows per sequence, a long key/value cache).
+//
+// Method: the same exact attention as fa_fwd, but the keys of each sequence
+// are cut into `num_splits` ranges that run in parallel. Each range produces a
+// partial output normalised by its own sum and a partial logsumexp; the
+// partials are merged with the blockwise rescaling rule of the Q-stationary
+// algorithm ("深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力" (rkmt.cn
+// blog) §2.2: when two parts of a row are combined, each is rescaled by the
+// exponential of its statistic minus the combined one). The split-KV idea for
+// decoding is named in the FlashDecoding paragraph of that blog's §3.
+//
+// gfx950 mapping
+// --------------
+//  * One workgroup (4 wave64s) per (batch, key/value head, key range). Its
+//    rows are the G = H_q/H_kv query heads of the group times the N_q queries
+//    (at most 32 rows, one MFMA column block): K and V are read once for all
+//    heads that share them.
+//  * The 4 waves take turns over 32-key tiles of the range and keep separate
+//    running (max, sum, O) states, merged through LDS at the end: no barrier
+//    inside the key loop. K goes from HBM straight into the MFMA A operand
+//    (S^T = K Q^T, lane = row); V goes through LDS by LDS-DMA and is read
+//    transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.
+//  * The work is HBM-bound: each key's K and V rows (512 bytes at d = 128)
+//    serve at most 32 rows. Many waves with a tile in flight each keep the
+//    memory system busy.
+//  * A second kernel merges the key ranges of every row in a fixed order
+//    (deterministic): LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+
+#include "fa_device.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kSplitWaves = 4;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+constexpr int kSplitBK = 32;  // keys per tile
+constexpr float kSplitRescaleSlack = 8.0f;  // log2 units
+
+template <int D>
+struct SplitCfg {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                       // rows per 1 KiB LDS-DMA instruction
+  static constexpr int TILE_BYTES = kSplitBK * ROW_BYTES;    // 8 KiB (d=128), 4 KiB (d=64)
+  static constexpr int NDMA = TILE_BYTES / 1024;             // DMA instructions per tile
+  static constexpr int KST = D / 16;                         // MFMA k-steps over d
+  static constexpr int DSUB = D / 32;                        // 32-column subtiles of O^T
+};
+
+// V tile chunk swizzle: a transposed-read phase reads 4 consecutive rows x 64
+// bytes; XOR-ing the chunk index with f(row) puts the 4 rows in different
+// 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz_split_v(int row) {
+  if constexpr (D == 128) return (row & 3) << 2;
+  else return ((row >> 1) & 1) << 2;
+}
+
+// Partial results of one key range: O_s normalised by the range's own sum
+// (float32, [row][D]) and LSE_s (natural log; -inf when the range has no key
+// visible to the row). With num_splits == 1 the final O (bf16) and LSE are
+// written instead.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart, float* __restrict__ Lpart,
+    int H_q, int H_kv, int N_q, int N_kv, int S, int keys_per_split, float c) {
+  using C = SplitCfg<D>;
+  // per wave: one V tile; reused at the end for the merge of the 4 waves
+  constexpr int kVBytes = kSplitWaves * C::TILE_BYTES;
+  constexpr int kMergeBytes = kSplitWaves * D * 32 * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+  __shared__ float ms[kSplitWaves][32], ls[kSplitWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;   // this lane's row (MFMA column)
+  const int half = lane >> 5;
+  const int G = H_q / H_kv;
+  const int R = G * N_q;       // rows of the workgroup (<= 32, checked by the host)
+
+  const int s = blockIdx.x % S;
+  const int bk = blockIdx.x / S;
+  const int b = bk / H_kv;
+  const int hk = bk % H_kv;
+
+  // this lane's row: query head hk*G + g, query i (lanes past R repeat row R-1)
+  const int r = min(col, R - 1);
+  const int g = r / N_q;
+  const int qi = r % N_q;
+  const int h = hk * G + g;
+  const size_t qrow_base = ((size_t(b) * H_q + h) * N_q + qi) * D;
+  bf16x8 qreg[C::KST];
+  {
+    const uint16_t* qp = Q + qrow_base + half * (D / 2);
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
+  }
+
+  // key range of this split; keys past the last visible one are never read
+  const int kb = s * keys_per_split;
+  int ke = min(N_kv, kb + keys_per_split);
+  if (CAUSAL) ke = min(ke, N_q);  // row i sees keys 0..i, and i < N_q
+  const int ntiles = ke > kb ? (ke - kb + kSplitBK - 1) / kSplitBK : 0;
+  // last key this lane's row may attend within the range
+  const int last_key = min(CAUSAL ? qi : N_kv - 1, ke - 1);
+
+  const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+  const uint16_t* Kh = K + kvbase;
+  const uint8_t* Vh = reinterpret_cast<const uint8_t*>(V + kvbase);
+  uint8_t* vt = lds + wave * C::TILE_BYTES;
+
+  // transposed-read offsets of V (as in the main forward kernel)
+  const int j16 = lane & 15;
+  const int vgrp = (lane & 31) >> 4;
+  int voff[C::DSUB];
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb) {
+    const int row = 16 * half + (j16 >> 2);
+    const int cc = 32 * sb + 16 * vgrp + 4 * (j16 & 3);
+    voff[sb] = row * C::ROW_BYTES + (((cc >> 3) ^ swz_split_v<D>(row)) * 16) + (cc & 7) * 2;
+  }
+  const int krow_lane = row_of_lane(col);
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 oacc[C::DSUB];
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb) oacc[sb] = f32x16{};
+
+  for (int tt = wave; tt < ntiles; tt += kSplitWaves) {
+    const int k0 = kb + tt * kSplitBK;
+    // K rows as the A operand (rows permuted so that accumulator register i of
+    // lane half g holds key 16g + i); rows past the end repeat the last key
+    bf16x8 ka[C::KST];
+    {
+      const uint16_t* kp = Kh + size_t(min(k0 + krow_lane, N_kv - 1)) * D + half * (D / 2);
+#pragma unroll
+      for (int t = 0; t < C::KST; ++t) ka[t] = as_bf16x8(ld_global16(kp + 8 * t));
+    }
+    // V tile into this wave's LDS buffer (swizzled 16-byte chunks)
+#pragma unroll
+    for (int ig = 0; ig < C::NDMA; ++ig) {
+      const int row = C::RPI * ig + lane / C::CPR;
+      const int pch = lane % C::CPR;
+      const int grow = min(k0 + row, N_kv - 1);
+      lds_dma16(Vh + size_t(grow) * C::ROW_BYTES + ((pch ^ swz_split_v<D>(row)) * 16),
+                (LDS_AS void*)(vt + 1024 * ig));
+    }
+    wait_vmem();
+
+    // S^T = K Q^T (keys x rows; lane = row)
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) sacc = mfma32x32x16(ka[t], qreg[t], sacc);
+    // key k0 + 16*half + i is visible iff i <= lim
+    const int lim = last_key - k0 - 16 * half;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i > lim) sacc[i] = -INFINITY;
+
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    const float m_blk = max_xor32(mx) * c;
+    // The running max is raised (and O, l rescaled) only when the tile's max
+    // exceeds it by more than 2^8; exact, since the final division and the
+    // logsumexp use the same, possibly stale, reference.
+    if (__any(m_blk > m_run + kSplitRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      // rows that have seen no visible key yet keep m = -inf (alpha = 1 then,
+      // nothing has been accumulated)
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[sb][i] *= alpha;
+      m_run = m_new;
+    }
+    // reference 0 for a row with no visible key so far: every exponential
+    // below is then exp2(-inf) = 0
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+
+    u32x4 pk[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(sacc[8 * u + e], c, -m_ref));
+        psum += p[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T (V read transposed from LDS)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rb = 8 * u * C::ROW_BYTES;
+#pragma unroll
+      for (int sb = 0; sb < C::DSUB; ++sb) {
+        const bf16x8 av = lds_read_tr8(vt + voff[sb] + rb, vt + voff[sb] + rb + 4 * C::ROW_BYTES);
+        oacc[sb] = mfma32x32x16(av, as_bf16x8(pk[u]), oacc[sb]);
+      }
+    }
+  }
+
+  // ---- merge the 4 waves: (m, l) per row and O^T (float32) through LDS
+  const float l_tot = sum_xor32(l_run);
+  __syncthreads();  // every wave is done with its V tile
+  float* om = reinterpret_cast<float*>(lds);  // [wave][d][row]
+  if (half == 0) {
+    ms[wave][col] = m_run;
+    ls[wave][col] = l_tot;
+  }
+  // accumulator register 4a+e of subtile sb holds d = 32 sb + 8a + 4 half + e
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        om[(wave * D + 32 * sb + 8 * a + 4 * half + e) * 32 + col] = oacc[sb][4 * a + e];
+  __syncthreads();
+
+  // each thread: one row and D/8 consecutive columns
+  constexpr int kColsPerThread = D * 32 / kSplitThreads;
+  const int mr = tid % 32;
+  const int d0 = (tid / 32) * kColsPerThread;
+  if (mr < R) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, ms[w][mr]);
+    float wgt[kSplitWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      wgt[w] = M == -INFINITY ? 0.f : fast_exp2(ms[w][mr] - M);
+      L += wgt[w] * ls[w][mr];
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    float ov[kColsPerThread];
+#pragma unroll
+    for (int j = 0; j < kColsPerThread; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSplitWaves; ++w) acc = fmaf(wgt[w], om[(w * D + d0 + j) * 32 + mr], acc);
+      ov[j] = acc * inv;
+    }
+    const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    const int gg = mr / N_q;
+    const int ii = mr % N_q;
+    const size_t row = (size_t(b) * H_q + hk * G + gg) * N_q + ii;
+    if (S == 1) {
+#pragma unroll
+      for (int j = 0; j < kColsPerThread; j += 4) {
+        u32x2 w2;
+        w2[0] = cvt_pk_bf16(ov[j], ov[j + 1]);
+        w2[1] = cvt_pk_bf16(ov[j + 2], ov[j + 3]);
+        st_global8(O + row * D + d0 + j, w2);
+      }
+      if (d0 == 0) LSE[row] = lse;
+    } else {
+      float* op = Opart + (row * S + s) * D + d0;
+#pragma unroll
+      for (int j = 0; j < kColsPerThread; j += 4) {
+        f32x4 v4;
+        v4[0] = ov[j];
+        v4[1] = ov[j + 1];
+        v4[2] = ov[j + 2];
+        v4[3] = ov[j + 3];
+        *reinterpret_cast<f32x4*>(op + j) = v4;
+      }
+      if (d0 == 0) Lpart[row * S + s] = lse;
+    }
+  }
+}
+
+// Merge of the key ranges of each row, in split order: one workgroup of D
+// threads per row, thread = output column.
+template <int D>
+__global__ __launch_bounds__(D) void fwd_split_combine_kernel(const float* __restrict__ Opart,
+                                                              const float* __restrict__ Lpart,
+                                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                              int S) {
+  const size_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* lp = Lpart + row * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  // every row sees key 0, so some range has a finite LSE_s and M is finite
+  float wsum = 0.f, acc = 0.f;
+  const float* op = Opart + row * S * D + d;
+  for (int s = 0; s < S; ++s) {
+    const float w = __expf(lp[s] - M);  // exp(-inf) = 0 for ranges without visible keys
+    wsum += w;
+    acc = fmaf(w, op[size_t(s) * D], acc);
+  }
+  const float o = acc / wsum;
+  // round to nearest even bf16 (one column per thread)
+  const uint32_t u = __float_as_uint(o);
+  O[row * D + d] = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  if (d == 0) LSE[row] = M + __logf(wsum);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdParams& p, int S, float* ws, hipStream_t stream) {
+  const int keys_per_split = ((p.N_kv + S - 1) / S + kSplitBK - 1) / kSplitBK * kSplitBK;
+  const long long rows = (long long)p.B * p.H_q * p.N_q;
+  float* Opart = ws;
+  float* Lpart = S > 1 ? ws + rows * S * D : nullptr;
+  const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
+  const long long nwg = (long long)p.B * p.H_kv * S;
+  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream,
+                     static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                     static_cast<const uint16_t*>(p.v), static_cast<uint16_t*>(p.o), p.lse, Opart, Lpart,
+                     p.H_q, p.H_kv, p.N_q, p.N_kv, S, keys_per_split, c);
+  if (S > 1)
+    hipLaunchKernelGGL((fwd_split_combine_kernel<D>), dim3((unsigned)rows), dim3(D), 0, stream, Opart, Lpart,
+                       static_cast<uint16_t*>(p.o), p.lse, S);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits) {
+  if (num_splits <= 1) return 0;
+  return size_t(B) * H_q * N_q * num_splits * (size_t(d) + 1);
+}
+
+hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* workspace, hipStream_t stream) {
+  if (p.d == 128)
+    return p.causal ? launch<128, true>(p, num_splits, workspace, stream)
+                    : launch<128, false>(p, num_splits, workspace, stream);
+  return p.causal ? launch<64, true>(p, num_splits, workspace, stream)
+                  : launch<64, false>(p, num_splits, workspace, stream);
+}
+
+}  // namespace fa

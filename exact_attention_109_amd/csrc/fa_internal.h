@@ -41,5 +41,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+// Split-KV forward (bf16, rows per key/value head <= 32); workspace holds
+// fwd_split_workspace_floats(...) floats when num_splits > 1.
+hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* workspace, hipStream_t stream);
+size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits);
 
 }  // namespace fa

@@ -119,6 +119,44 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H_q, int H_kv, int N_q, int N_kv, int d,
            int causal, float scale, int dtype, void* stream);
 
+/*
+ * fa_fwd_splitkv_workspace_size -- bytes of device workspace fa_fwd_splitkv
+ * needs: 0 for num_splits <= 1, else B*H_q*N_q*num_splits*(d+1) float32
+ * values (a partial output row and a partial logsumexp per key range),
+ * rounded up to a multiple of 256. Returns 0 for non-positive sizes.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv -- attention forward for few query rows against many keys
+ * (decode-like shapes), with the keys of every (batch, key/value head) cut
+ * into num_splits consecutive ranges processed in parallel and merged.
+ *
+ * Computes the same o and lse as fa_fwd (same arguments, conventions and
+ * layouts). Method: "深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力"
+ * (rkmt.cn blog) §2.2 -- each key range yields an output normalised by its
+ * own sum and a logsumexp; ranges are merged by rescaling each with the
+ * exponential of its logsumexp minus the combined one (the same rule that
+ * merges consecutive key blocks), in range order, so results are
+ * deterministic. Key ranges hold ceil(N_kv/num_splits) keys rounded up to a
+ * multiple of 32; ranges past the end (or past the last key any row may
+ * attend, when causal) contribute nothing.
+ *
+ * Restrictions beyond fa_fwd: dtype must be FA_DTYPE_BF16 (else
+ * FA_ERR_UNSUPPORTED); the rows of one key/value head, (H_q/H_kv)*N_q, must
+ * be at most 32 (else FA_ERR_UNSUPPORTED; use fa_fwd); 1 <= num_splits <= 256
+ * (else FA_ERR_INVALID_ARG). workspace: device memory of at least
+ * fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits) bytes, 16-byte
+ * aligned, not overlapping any other argument (may be NULL when that size is
+ * 0); its content on entry does not matter and on return is unspecified.
+ * Argument checks happen in the order of fa_fwd, then num_splits, dtype and
+ * the row count, then the workspace.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                   int causal, float scale, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_status_string -- a static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

@@ -27,8 +27,9 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_status_string"]
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_size", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -137,3 +138,54 @@ def test_workspace_too_small_is_rejected():
     assert bwd_call(workspace_bytes=0) == INVALID
     need = fa.fa_bwd_workspace_size(1, 2, 16)
     assert bwd_call(workspace_bytes=need - 1) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# split-KV forward
+# ---------------------------------------------------------------------------
+
+def split_call(**kw):
+    q, k, v, o, lse, ws = ptrs(6)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, B=1, H_q=8, H_kv=2, N_q=1, N_kv=1000, d=128, causal=0,
+                scale=0.088, dtype=fa.FA_DTYPE_BF16, num_splits=4, workspace=ws, workspace_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv(**args)
+
+
+def test_splitkv_workspace_size():
+    # B*H_q*N_q*S*(d+1) floats, rounded up to 256 bytes; 0 without splitting
+    assert fa.fa_fwd_splitkv_workspace_size(2, 32, 1, 128, 8) == 2 * 32 * 1 * 8 * 129 * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 64, 2) == 768
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 3, 64, 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(0, 4, 3, 64, 4) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 5, 128, 3) % 256 == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(dtype=7), UNSUP),
+    (dict(d=96), UNSUP),
+    (dict(H_kv=3, H_q=8), INVALID),
+    (dict(N_kv=0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=-1.0), UNSUP),
+    (dict(q=0), INVALID),
+    (dict(o=A), INVALID),                       # o aliases q
+    (dict(num_splits=0), INVALID),
+    (dict(num_splits=257), INVALID),
+    (dict(dtype=fa.FA_DTYPE_F32), UNSUP),       # bf16 only
+    (dict(H_q=64, H_kv=1, N_q=1), UNSUP),       # 64 rows per key/value head
+    (dict(H_q=8, H_kv=1, N_q=5), UNSUP),        # 40 rows
+    (dict(workspace=0), INVALID),
+    (dict(workspace=A + 8), INVALID),           # misaligned
+    (dict(workspace_bytes=10), INVALID),
+    (dict(workspace=A + 2 * STEP), INVALID),    # workspace aliases v
+])
+def test_splitkv_invalid_arguments(kw, expect):
+    assert split_call(**kw) == expect
+
+
+def test_splitkv_empty_and_unsplit_workspace():
+    assert split_call(N_q=0) == fa.FA_OK
+    assert split_call(B=0, workspace=0, workspace_bytes=0) == fa.FA_OK

@@ -1,0 +1,123 @@
+"""Split-KV forward (fa_fwd_splitkv) on the GPU: parity with the fp64 CPU
+oracle on identical bf16 inputs, agreement with fa_fwd, closed forms and
+determinism. Decode-like shapes: few query rows per key/value head, many
+keys, key ranges that are partial, empty or past the causal limit."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import TOL, default_scale, ensure_library, max_abs, o_within, to_f64, upload
+from workloads import DECODE_WORKLOADS, DTYPE_BF16, make_inputs, make_inputs_shape
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_library()
+
+
+def run_split(inp, causal, scale, splits):
+    import exact_attention_109_amd as fa
+    import torch
+    q, k, v = upload(inp)
+    o, lse = fa.fwd_splitkv(q, k, v, splits, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+# (B, H_q, H_kv, N_q, N_kv, d, causal, num_splits)
+CASES = [
+    (1, 1, 1, 1, 1, 128, False, 1),
+    (1, 1, 1, 1, 1, 64, False, 4),          # more ranges than keys
+    (2, 8, 2, 1, 1000, 128, False, 4),
+    (1, 32, 8, 1, 4097, 128, False, 16),    # ragged last range
+    (1, 8, 8, 1, 300, 64, False, 7),
+    (2, 4, 4, 3, 517, 64, True, 3),         # causal: keys past the rows are never read
+    (1, 8, 1, 4, 2048, 64, False, 8),       # 32 rows per key/value head (the maximum)
+    (1, 4, 1, 2, 100, 128, True, 2),
+    (1, 16, 2, 1, 33, 128, False, 256),     # 256 ranges, all but two empty
+    (3, 6, 2, 5, 777, 128, False, 5),
+    (1, 2, 1, 16, 64, 128, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nkv{c[4]}d{c[5]}{'c' if c[6] else 'n'}S{c[7]}" for c in CASES])
+def test_against_oracle(case):
+    B, Hq, Hkv, nq, nkv, d, causal, S = case
+    print(f"case {case}", flush=True)
+    inp = make_inputs_shape(DTYPE_BF16, B, Hq, Hkv, nq, nkv, d, seed=700 + sum(case[:6]))
+    scale = default_scale(d)
+    o, lse = run_split(inp, causal, scale, S)
+    O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), causal, scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert o_within(o, O, DTYPE_BF16), max_abs(o, O)
+    assert max_abs(lse, L) <= TOL[DTYPE_BF16]["lse"], max_abs(lse, L)
+
+
+def test_agrees_with_fa_fwd_for_every_split_count():
+    import exact_attention_109_amd as fa
+    import torch
+    inp = make_inputs_shape(DTYPE_BF16, 2, 16, 4, 2, 3000, 128, seed=811)
+    q, k, v = upload(inp)
+    o_ref, l_ref = fa.fwd(q, k, v, causal=False)
+    O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), False, default_scale(128))
+    for S in (1, 2, 3, 8, 31, 94, 200):
+        o, lse = fa.fwd_splitkv(q, k, v, S)
+        torch.cuda.synchronize()
+        # both are within the tolerance of the exact result, hence within twice of each other
+        assert o_within(to_f64(o), O, DTYPE_BF16), S
+        assert max_abs(to_f64(lse), to_f64(l_ref)) <= 2 * TOL[DTYPE_BF16]["lse"], S
+        assert max_abs(to_f64(o), to_f64(o_ref)) <= 2 * TOL[DTYPE_BF16]["o"] + 2 ** -7, S
+
+
+def test_zero_queries_give_uniform_weights():
+    # Q = 0: every allowed key has weight 1/count, so O is the mean of the
+    # allowed V rows and LSE = ln(count) (closed form, no oracle needed)
+    import exact_attention_109_amd as fa
+    import torch
+    B, Hq, Hkv, nq, nkv, d = 1, 4, 2, 3, 1234, 128
+    inp = make_inputs_shape(DTYPE_BF16, B, Hq, Hkv, nq, nkv, d, seed=812)
+    q, k, v = upload(inp)
+    q.zero_()
+    V = inp.f64("v")
+    for causal in (False, True):
+        o, lse = fa.fwd_splitkv(q, k, v, 6, causal=causal)
+        torch.cuda.synchronize()
+        o, lse = to_f64(o), to_f64(lse)
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(nq):
+                    n_allowed = (i + 1) if causal else nkv
+                    ref = V[b, h // (Hq // Hkv), :n_allowed].mean(axis=0)
+                    assert o_within(o[b, h, i], ref, DTYPE_BF16)
+                    assert abs(lse[b, h, i] - np.log(n_allowed)) <= 1e-3
+
+
+def test_deterministic():
+    import exact_attention_109_amd as fa
+    import torch
+    inp = make_inputs_shape(DTYPE_BF16, 2, 8, 2, 1, 5000, 128, seed=813)
+    q, k, v = upload(inp)
+    a = fa.fwd_splitkv(q, k, v, 12)
+    b = fa.fwd_splitkv(q, k, v, 12)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_workload_every_row():
+    # the benchmark's decode shape at full size: every one of the B*H_q rows
+    # against the oracle (one row per head keeps the oracle cheap)
+    import exact_attention_109_amd as fa
+    import torch
+    w = DECODE_WORKLOADS["d1"]
+    inp = make_inputs(w)
+    q, k, v = upload(inp)
+    o, lse = fa.fwd_splitkv(q, k, v, 16, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.causal, w.scale)
+    assert o_within(to_f64(o), O, DTYPE_BF16), max_abs(to_f64(o), O)
+    assert max_abs(to_f64(lse), L) <= TOL[DTYPE_BF16]["lse"]

@@ -67,6 +67,14 @@ WORKLOADS = {
 }
 
 
+# Decode-like shapes for the split-KV forward: one new query row per
+# sequence against a long key/value cache, GQA with 4 query heads per
+# key/value head (not one of the five configurations above).
+DECODE_WORKLOADS = {
+    "d1": Workload("d1_bf16_decode_gqa_kv32768_d128", DTYPE_BF16, 8, 32, 8, 1, 32768, 128, False, 6),
+}
+
+
 # ---------------------------------------------------------------------------
 # bf16 bit handling (exact; round-to-nearest-even)
 # ---------------------------------------------------------------------------
