@@ -26,7 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import DECODE_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
+from workloads import (DECODE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, cu_seqlens,  # noqa: E402
+                       make_inputs, make_packed_inputs)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3
@@ -183,6 +184,45 @@ def time_decode(fa, torch, steps: int):
     }
 
 
+def time_varlen(fa, torch, steps: int):
+    """Packed variable-length forward: TFLOP/s over the sum of the per-sequence
+    FLOP counts (4*H_q*n^2*d, halved when causal)."""
+    w = VARLEN_WORKLOADS["v1"]
+    lengths = w.lengths()
+    total = int(lengths.sum())
+    inp = make_packed_inputs(1, w.H_q, w.H_kv, total, total, w.d, w.seed)
+    q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+    cu = torch.from_numpy(cu_seqlens(lengths)).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.H_q, total), dtype=torch.float32, device="cuda")
+    mx = int(lengths.max())
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < 0.5:
+        fa.fwd_varlen(q, k, v, cu, cu, mx, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        n += 1
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in per:
+        a.record(stream)
+        fa.fwd_varlen(q, k, v, cu, cu, mx, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in per]
+    med = float(np.median(ms))
+    tf = w.fwd_flop() / (med * 1e-3) / 1e12
+    return {
+        "workload": w.name,
+        "entry_point": "fa_fwd_varlen",
+        "lengths": [int(x) for x in lengths],
+        "median_ms": round(med, 4),
+        "min_ms": round(float(np.min(ms)), 4),
+        "tflops": round(tf, 2),
+        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +235,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement on c5")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
@@ -308,6 +349,9 @@ def main():
     if not args.no_bwd:
         print("# timing the backward on c5", file=sys.stderr, flush=True)
         result["bwd"] = time_backward(fa, torch, max(3, args.steps // 2), 2)
+    if not args.no_varlen:
+        print("# timing the packed variable-length forward", file=sys.stderr, flush=True)
+        result["varlen"] = time_varlen(fa, torch, max(5, args.steps // 2))
     if not args.no_decode:
         print("# timing the split-KV forward on the decode workload", file=sys.stderr, flush=True)
         result["decode"] = time_decode(fa, torch, max(5, args.steps))

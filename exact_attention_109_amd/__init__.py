@@ -1,13 +1,14 @@
 """Exact attention on AMD MI355X (gfx950): Python binding of libfa.so.
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
-fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size and
-fa_status_string. This module exposes the same names with the same
+fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
+fa_fwd_varlen and fa_status_string. This module exposes the same names with the same
 arguments (device pointers as integers, sizes, flags, a stream handle) plus
 convenience wrappers over torch tensors:
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
     o, lse = fwd_splitkv(q, k, v, num_splits, causal=False, scale=None)
+    o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
 
 The wrappers only marshal arguments: torch allocates device memory and
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_size.restype = sz
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -94,6 +97,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, d
 
 def fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits) -> int:
     return load_library().fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, H_q,
+                  H_kv, d, causal, scale, dtype, stream) -> int:
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k,
+                                        max_seqlen_q, H_q, H_kv, d, int(causal), float(scale), dtype, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -196,6 +205,36 @@ def fwd_splitkv(q, k, v, num_splits: int | None = None, causal: bool = False, sc
     return out, lse
 
 
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+               scale: float | None = None, out=None, lse=None):
+    """Forward over packed sequences: q [H_q, total_q, d], k and v
+    [H_kv, total_k, d] (bf16), cu_seqlens_* int32 GPU tensors of num_seqs + 1
+    prefix offsets. Returns (o like q, lse float32 [H_q, total_q])."""
+    import torch
+    H_q, total_q, d = q.shape
+    H_kv, total_k, _ = k.shape
+    _check(q, "q")
+    _check(k, "k", q.dtype, (H_kv, total_k, d))
+    _check(v, "v", q.dtype, (H_kv, total_k, d))
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, cu_seqlens_q.shape)
+    num_seqs = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H_q, total_q), dtype=torch.float32, device=q.device)
+    _check(out, "out", q.dtype, q.shape)
+    _check(lse, "lse", torch.float32, (H_q, total_q))
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), num_seqs, total_q, total_k, max_seqlen_q,
+                       H_q, H_kv, d, causal, scale, _dtype_code(q), _stream_handle(q))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_varlen")
+    return out, lse
+
+
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
     """Attention backward; o and lse from fwd on the same inputs.
 
@@ -226,6 +265,6 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
 
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_status_string", "fwd", "fwd_splitkv", "default_num_splits", "bwd", "load_library",
+           "fa_fwd_varlen", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
            "FA_DTYPE_BF16", "LIB_PATH"]

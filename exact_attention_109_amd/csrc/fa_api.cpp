@@ -215,3 +215,44 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* 
                                              reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                            int total_q, int total_k, int max_seqlen_q,
+                            int H_q, int H_kv, int d, int causal, float scale, int dtype, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || H_q < 0 || H_kv < 0 || d < 0)
+    return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || H_q == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;
+  if (H_kv == 0 || H_q % H_kv != 0) return FA_ERR_INVALID_ARG;
+  if (total_k == 0) return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > kMaxSeq) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
+
+  const size_t q_bytes = size_t(H_q) * total_q * d * 2;
+  const size_t kv_bytes = size_t(H_kv) * total_k * d * 2;
+  const size_t lse_bytes = size_t(H_q) * total_q * sizeof(float);
+  const size_t cu_bytes = (size_t(num_seqs) + 1) * sizeof(int);
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  const Range in[5] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(v, kv_bytes),
+                       range_of(cu_seqlens_q, cu_bytes), range_of(cu_seqlens_k, cu_bytes)};
+  const Range out[2] = {range_of(o, q_bytes), range_of(lse, lse_bytes)};
+  for (const Range& r : out)
+    for (const Range& i : in)
+      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
+
+  int rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::FwdParams p{q, k, v, o, lse, num_seqs, H_q, H_kv, max_seqlen_q, 0, d, causal ? 1 : 0, scale};
+  fa::VarlenParams vl{cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  hipError_t err = fa::launch_fwd_varlen_bf16(p, vl, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -100,7 +100,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, float c) {
+    int H_q, int H_kv, int N_q_arg, int N_kv_arg, int n_qtiles, int xcd_remap, float c,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
   constexpr int NSUB = C::NSUB;
@@ -130,8 +131,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tile = CAUSAL ? (n_qtiles - 1 - tile_rank) : tile_rank;  // heaviest first
   const int q0 = tile * kBR;
 
-  const size_t qbase = (size_t(b) * H_q + h) * size_t(N_q) * D;
-  const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+  // Dense: q, o [B][H_q][N_q][D], k, v [B][H_kv][N_kv][D], lse [B][H_q][N_q].
+  // Packed sequences (cu_q != null): b is a sequence, q, o [H_q][total_q][D],
+  // k, v [H_kv][total_k][D], lse [H_q][total_q]; sequence b owns rows
+  // cu_q[b] .. cu_q[b+1]-1 of q and cu_k[b] .. cu_k[b+1]-1 of k. The offsets
+  // are clamped to [0, total], so inconsistent ones give wrong rows, never an
+  // access outside the tensors; N_q_arg is then the longest query sequence
+  // the grid covers.
+  int N_q = N_q_arg, N_kv = N_kv_arg;
+  size_t qbase, kvbase, lbase;
+  if (cu_q != nullptr) {
+    const int qs = min(max(cu_q[b], 0), total_q);
+    const int qe = min(max(cu_q[b + 1], qs), total_q);
+    const int ks = min(max(cu_k[b], 0), total_k);
+    const int ke = min(max(cu_k[b + 1], ks), total_k);
+    N_q = min(qe - qs, N_q_arg);
+    N_kv = ke - ks;
+    qbase = (size_t(h) * total_q + qs) * D;
+    kvbase = (size_t(hk) * total_k + ks) * D;
+    lbase = size_t(h) * total_q + qs;
+  } else {
+    qbase = (size_t(b) * H_q + h) * size_t(N_q) * D;
+    kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+    lbase = (size_t(b) * H_q + h) * size_t(N_q);
+  }
+  if (q0 >= N_q) return;  // (whole workgroup) a tile past a short sequence
+  if (N_kv == 0) {
+    // a sequence without keys: softmax over nothing; its rows get O = 0 and
+    // LSE = -inf (packed sequences only, dense calls reject N_kv = 0)
+    const int row = q0 + wave * 32 + col;
+    if (row < N_q) {
+      uint16_t* op = O + qbase + size_t(row) * D + half * (D / 2);
+#pragma unroll
+      for (int j = 0; j < D / 2; j += 4) st_global8(op + j, u32x2{0u, 0u});
+      if (half == 0) LSE[lbase + row] = -INFINITY;
+    }
+    return;
+  }
   const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
   const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
 
@@ -447,12 +483,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         st_global8(op + 32 * s + 8 * a + 4 * half, w);
       }
     }
-    if (half == 0) LSE[(size_t(b) * H_q + h) * size_t(N_q) + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (half == 0) LSE[lbase + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
+// Dense when vl is null; packed sequences otherwise (p.B sequences, p.N_q the
+// longest query sequence).
 template <int D, bool CAUSAL>
-hipError_t launch(const FwdParams& p, hipStream_t stream) {
+hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream) {
   const int n_qtiles = (p.N_q + kBR - 1) / kBR;
   const long long nwg = (long long)n_qtiles * p.B * p.H_q;
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
@@ -463,15 +501,22 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<uint16_t*>(p.o), p.lse,
-                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c);
+                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c,
+                     vl ? vl->cu_q : nullptr, vl ? vl->cu_k : nullptr, vl ? vl->total_q : 0,
+                     vl ? vl->total_k : 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 128) return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-  return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (p.d == 128) return p.causal ? launch<128, true>(p, nullptr, stream) : launch<128, false>(p, nullptr, stream);
+  return p.causal ? launch<64, true>(p, nullptr, stream) : launch<64, false>(p, nullptr, stream);
+}
+
+hipError_t launch_fwd_varlen_bf16(const FwdParams& p, const VarlenParams& vl, hipStream_t stream) {
+  if (p.d == 128) return p.causal ? launch<128, true>(p, &vl, stream) : launch<128, false>(p, &vl, stream);
+  return p.causal ? launch<64, true>(p, &vl, stream) : launch<64, false>(p, &vl, stream);
 }
 
 }  // namespace fa

@@ -35,10 +35,21 @@ struct BwdParams {
   float scale;
 };
 
+// Packed variable-length sequences: sequence b owns query rows
+// cu_q[b] .. cu_q[b+1]-1 of the [H_q][total_q][d] tensors and key rows
+// cu_k[b] .. cu_k[b+1]-1 of the [H_kv][total_k][d] ones (device int32 arrays).
+struct VarlenParams {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+};
+
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 // The front end has already validated every argument.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+// p.B = number of sequences, p.N_q = longest query sequence, p.N_kv unused
+hipError_t launch_fwd_varlen_bf16(const FwdParams& p, const VarlenParams& vl, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
 // Split-KV forward (bf16, rows per key/value head <= 32); workspace holds

@@ -157,6 +157,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, float scale, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_fwd_varlen -- attention forward over a batch of sequences of different
+ * lengths, packed without padding.
+ *
+ * Layouts (head-major, sequences packed along the row axis):
+ *     q, o : [H_q][total_q][d]      k, v : [H_kv][total_k][d]
+ *     lse  : [H_q][total_q]          (float32, natural log)
+ * cu_seqlens_q, cu_seqlens_k: DEVICE int32 arrays of num_seqs + 1 prefix
+ * offsets: sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (first entry 0,
+ * non-decreasing, last entry total_q / total_k). max_seqlen_q must be at
+ * least the longest query sequence (rows past it are not computed).
+ * Within each sequence the operation is exactly that of fa_fwd (same scale,
+ * causal rule counted from the sequence's first row and key, GQA mapping).
+ * A sequence with no keys gets o = 0 and lse = -inf on its rows.
+ * The offsets are read on the device and not validated on the host; offsets
+ * outside [0, total] are clamped, so inconsistent ones give wrong rows but no
+ * access outside the tensors.
+ *
+ * dtype must be FA_DTYPE_BF16 (else FA_ERR_UNSUPPORTED). Argument checks
+ * before any HIP call: negative sizes (FA_ERR_INVALID_ARG); dtype and d;
+ * empty problem (num_seqs, H_q, total_q or max_seqlen_q zero -> FA_OK);
+ * H_kv; total_k = 0 (FA_ERR_INVALID_ARG); max_seqlen_q > 2^24; scale; null or
+ * misaligned pointers (16 bytes; 4 for the offset arrays); an output
+ * overlapping an input or the other output.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                  int total_q, int total_k, int max_seqlen_q,
+                  int H_q, int H_kv, int d, int causal, float scale, int dtype, void* stream);
+
 /* fa_status_string -- a static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_size", "fa_status_string"]
+                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -189,3 +189,42 @@ def test_splitkv_invalid_arguments(kw, expect):
 def test_splitkv_empty_and_unsplit_workspace():
     assert split_call(N_q=0) == fa.FA_OK
     assert split_call(B=0, workspace=0, workspace_bytes=0) == fa.FA_OK
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length forward
+# ---------------------------------------------------------------------------
+
+def varlen_call(**kw):
+    q, k, v, o, lse, cq, ck = ptrs(7)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, cu_seqlens_q=cq, cu_seqlens_k=ck, num_seqs=3, total_q=100,
+                total_k=120, max_seqlen_q=60, H_q=4, H_kv=2, d=128, causal=1, scale=0.088,
+                dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_varlen(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_seqs=-1), INVALID),
+    (dict(total_q=-5), INVALID),
+    (dict(dtype=fa.FA_DTYPE_F32), UNSUP),
+    (dict(dtype=9), UNSUP),
+    (dict(d=32), UNSUP),
+    (dict(H_kv=3), INVALID),
+    (dict(total_k=0), INVALID),
+    (dict(max_seqlen_q=(1 << 24) + 1), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(scale=-2.0), UNSUP),
+    (dict(cu_seqlens_q=0), INVALID),
+    (dict(cu_seqlens_k=A + 6 * STEP + 2), INVALID),     # not 4-byte aligned
+    (dict(o=A + 5 * STEP), INVALID),                    # o overlaps the query offsets
+    (dict(lse=A + 2 * STEP + 64), INVALID),             # lse inside v
+])
+def test_varlen_invalid_arguments(kw, expect):
+    assert varlen_call(**kw) == expect
+
+
+def test_varlen_empty_is_a_noop():
+    assert varlen_call(num_seqs=0) == fa.FA_OK
+    assert varlen_call(total_q=0, q=0, o=0, lse=0) == fa.FA_OK
+    assert varlen_call(max_seqlen_q=0) == fa.FA_OK

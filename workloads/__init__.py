@@ -177,3 +177,60 @@ def make_inputs_shape(dtype, B, H_q, H_kv, N_q, N_kv, d, seed, with_grad=False,
 def make_inputs(w: Workload) -> Inputs:
     return make_inputs_shape(w.dtype, w.B, w.H_q, w.H_kv, w.N_q, w.N_kv, w.d, w.seed,
                              with_grad=w.with_grad, qk_multiplier=w.qk_multiplier)
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length sequences
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A batch of sequences of different lengths, packed head-major without
+    padding: q [H_q, total_q, d], k and v [H_kv, total_k, d]. Query and key
+    lengths are equal per sequence (self-attention), drawn uniformly from
+    [min_len, max_len] by the seed."""
+    name: str
+    num_seqs: int
+    min_len: int
+    max_len: int
+    H_q: int
+    H_kv: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.Generator(np.random.PCG64(self.seed + 1000))
+        return rng.integers(self.min_len, self.max_len + 1, size=self.num_seqs).astype(np.int64)
+
+    def fwd_flop(self) -> float:
+        """4*H_q*n^2*d per sequence of length n, halved when causal."""
+        f = sum(4.0 * self.H_q * float(n) * float(n) * self.d for n in self.lengths())
+        return f / 2.0 if self.causal else f
+
+
+VARLEN_WORKLOADS = {
+    "v1": VarlenWorkload("v1_bf16_causal_varlen_16seq_512to8192_d128", 16, 512, 8192, 32, 8, 128, True, 7),
+}
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Prefix offsets [0, l0, l0+l1, ...] as int32."""
+    out = np.zeros(len(lengths) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return out.astype(np.int32)
+
+
+def make_packed_inputs(dtype, H_q, H_kv, total_q, total_k, d, seed) -> Inputs:
+    """q [H_q, total_q, d], k and v [H_kv, total_k, d]: i.i.d. N(0,1) drawn in
+    that order from PCG64(seed), rounded to bf16 for DTYPE_BF16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    arrays = {"q": _draw(rng, (H_q, total_q, d)), "k": _draw(rng, (H_kv, total_k, d)),
+              "v": _draw(rng, (H_kv, total_k, d))}
+    if dtype == DTYPE_BF16:
+        arrays = {n: f32_to_bf16_bits(a) for n, a in arrays.items()}
+    return Inputs(dtype, arrays)
