@@ -2,13 +2,14 @@
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
 fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
-fa_fwd_varlen and fa_status_string. This module exposes the same names with the same
+fa_fwd_varlen, fa_fwd_check and fa_status_string. This module exposes the same names with the same
 arguments (device pointers as integers, sizes, flags, a stream handle) plus
 convenience wrappers over torch tensors:
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
     o, lse = fwd_splitkv(q, k, v, num_splits, causal=False, scale=None)
     o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, scale=None)
+    err = fwd_check(q, k, lse, rows, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
 
 The wrappers only marshal arguments: torch allocates device memory and
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_workspace_size.restype = sz
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, vp]
+    lib.fa_fwd_check.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -103,6 +106,11 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q
                   H_kv, d, causal, scale, dtype, stream) -> int:
     return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k,
                                         max_seqlen_q, H_q, H_kv, d, int(causal), float(scale), dtype, stream)
+
+
+def fa_fwd_check(q, k, lse, rows, n_rows, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, result, stream) -> int:
+    return load_library().fa_fwd_check(q, k, lse, rows, n_rows, B, H_q, H_kv, N_q, N_kv, d, int(causal),
+                                       float(scale), dtype, result, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -235,6 +243,27 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: b
     return out, lse
 
 
+def fwd_check(q, k, lse, rows, causal: bool = False, scale: float | None = None):
+    """Self-check of a forward result: |sum_j exp(scale q_i.k_j - lse_i) - 1|
+    for the query rows `rows` (int32 GPU tensor) of every (batch, head).
+    Returns a float32 tensor [B, H_q, len(rows)]."""
+    import torch
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k.shape
+    _check(q, "q")
+    _check(k, "k", q.dtype, (B, H_kv, N_kv, d))
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    _check(rows, "rows", torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    result = torch.empty((B, H_q, rows.numel()), dtype=torch.float32, device=q.device)
+    rc = fa_fwd_check(q.data_ptr(), k.data_ptr(), lse.data_ptr(), rows.data_ptr(), rows.numel(), B, H_q, H_kv,
+                      N_q, N_kv, d, causal, scale, _dtype_code(q), result.data_ptr(), _stream_handle(q))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_check")
+    return result
+
+
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
     """Attention backward; o and lse from fwd on the same inputs.
 
@@ -265,6 +294,6 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
 
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_fwd_varlen", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "default_num_splits", "bwd", "load_library",
+           "fa_fwd_varlen", "fa_fwd_check", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "fwd_check", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
            "FA_DTYPE_BF16", "LIB_PATH"]

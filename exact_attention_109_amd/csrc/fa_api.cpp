@@ -256,3 +256,35 @@ FA_EXPORT int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o
   hipError_t err = fa::launch_fwd_varlen_bf16(p, vl, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+FA_EXPORT int fa_fwd_check(const void* q, const void* k, const float* lse, const int* rows, int n_rows,
+                           int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                           float* result, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  if (n_rows < 0) return FA_ERR_INVALID_ARG;
+  if (n_rows == 0) return FA_OK;
+
+  const size_t es = elem_size(dtype);
+  const size_t q_bytes = size_t(B) * H_q * N_q * d * es;
+  const size_t kv_bytes = size_t(B) * H_kv * N_kv * d * es;
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  const size_t rows_bytes = size_t(n_rows) * sizeof(int);
+  const size_t res_bytes = size_t(B) * H_q * n_rows * sizeof(float);
+  if (!q || !k || !lse || !rows || !result) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(lse) || !aligned16(result)) return FA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(rows) & 3u) return FA_ERR_INVALID_ARG;
+  const Range in[4] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(lse, lse_bytes),
+                       range_of(rows, rows_bytes)};
+  const Range out = range_of(result, res_bytes);
+  for (const Range& i : in)
+    if (overlaps(out, i)) return FA_ERR_INVALID_ARG;
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::FwdParams p{q, k, nullptr, nullptr, const_cast<float*>(lse), B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipError_t err = fa::launch_check(p, rows, n_rows, result, dtype, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

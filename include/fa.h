@@ -188,6 +188,26 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int total_q, int total_k, int max_seqlen_q,
                   int H_q, int H_kv, int d, int causal, float scale, int dtype, void* stream);
 
+/*
+ * fa_fwd_check -- on-GPU self-check of a forward result. For each batch b,
+ * query head h and each of the n_rows sampled query rows i = rows[r]
+ * (DEVICE int32 array; values are clamped to [0, N_q-1]):
+ *     result[b][h][r] = | sum_j exp(scale * <q[b,h,i,:], k[b,h_kv,j,:]> - lse[b,h,i]) - 1 |
+ * over the keys row i may attend (float32, DEVICE array [B][H_q][n_rows]).
+ * With the lse of fa_fwd the probabilities of every row sum to one, so each
+ * value is near 0 (about the lse tolerance, 1e-3 for bf16); a corrupted
+ * statistic shows up directly ("Flash-Attention" (Awesome System Papers Wiki),
+ * core-idea section: the backward pass rebuilds the probabilities from these
+ * statistics). The scores are recomputed with plain fp32 dot products,
+ * independently of the forward kernels; deterministic.
+ * q, k, lse: as for fa_fwd (dtype F32 or BF16). n_rows = 0 (or an empty
+ * problem) is a no-op. Argument checks as fa_fwd, then n_rows < 0, null or
+ * misaligned rows (4 bytes) / result (16 bytes), result overlapping an input.
+ */
+int fa_fwd_check(const void* q, const void* k, const float* lse, const int* rows, int n_rows,
+                 int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, int dtype,
+                 float* result, void* stream);
+
 /* fa_status_string -- a static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

@@ -28,8 +28,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_check", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -228,3 +229,36 @@ def test_varlen_empty_is_a_noop():
     assert varlen_call(num_seqs=0) == fa.FA_OK
     assert varlen_call(total_q=0, q=0, o=0, lse=0) == fa.FA_OK
     assert varlen_call(max_seqlen_q=0) == fa.FA_OK
+
+
+# ---------------------------------------------------------------------------
+# self-check
+# ---------------------------------------------------------------------------
+
+def check_call(**kw):
+    q, k, lse, rows, res = ptrs(5)
+    args = dict(q=q, k=k, lse=lse, rows=rows, n_rows=4, B=1, H_q=2, H_kv=1, N_q=16, N_kv=16, d=64, causal=0,
+                scale=0.125, dtype=fa.FA_DTYPE_BF16, result=res, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_check(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(dtype=5), UNSUP),
+    (dict(d=48), UNSUP),
+    (dict(n_rows=-1), INVALID),
+    (dict(rows=0), INVALID),
+    (dict(rows=A + 3 * STEP + 2), INVALID),   # not 4-byte aligned
+    (dict(result=A + 4 * STEP + 4), INVALID),  # not 16-byte aligned
+    (dict(result=A + 8), INVALID),             # result inside q (and misaligned)
+    (dict(result=A + STEP), INVALID),          # result == k
+    (dict(scale=float("nan")), INVALID),
+])
+def test_check_invalid_arguments(kw, expect):
+    assert check_call(**kw) == expect
+
+
+def test_check_noop():
+    assert check_call(n_rows=0) == fa.FA_OK
+    assert check_call(N_q=0) == fa.FA_OK
