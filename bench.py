@@ -171,6 +171,21 @@ def time_decode(fa, torch, steps: int):
     ms = [a.elapsed_time(b) for a, b in per]
     med = float(np.median(ms))
     gbs = nbytes / (med * 1e-3) / 1e9
+    # context: a plain device-to-device copy of 512 MiB (read + write bytes)
+    src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
     return {
         "workload": w.name,
         "entry_point": "fa_fwd_splitkv",
@@ -181,6 +196,7 @@ def time_decode(fa, torch, steps: int):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(gbs / 8000.0, 4)},
         "tflops": round(w.fwd_flop / (med * 1e-3) / 1e12, 2),
+        "device_copy_gbs": round(copy_gbs, 1),
     }
 
 

@@ -18,9 +18,10 @@
 //    heads that share them.
 //  * The 4 waves take turns over 32-key tiles of the range and keep separate
 //    running (max, sum, O) states, merged through LDS at the end: no barrier
-//    inside the key loop. K goes from HBM straight into the MFMA A operand
-//    (S^T = K Q^T, lane = row); V goes through LDS by LDS-DMA and is read
-//    transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.
+//    inside the key loop. K and V go through LDS by LDS-DMA (fully coalesced
+//    1 KiB pieces); K is read by rows as the A operand of S^T = K Q^T
+//    (lane = row), V transposed (ds_read_b64_tr_b16) as the A operand of
+//    O^T += V^T P^T.
 //  * The work is HBM-bound: each key's K and V rows (512 bytes at d = 128)
 //    serve at most 32 rows. Many waves with a tile in flight each keep the
 //    memory system busy.
@@ -49,9 +50,16 @@ struct SplitCfg {
   static constexpr int DSUB = D / 32;                        // 32-column subtiles of O^T
 };
 
-// V tile chunk swizzle: a transposed-read phase reads 4 consecutive rows x 64
-// bytes; XOR-ing the chunk index with f(row) puts the 4 rows in different
-// 64-byte bank groups.
+// Tile chunk swizzles (16-byte chunk index XOR f(row)).
+//  K: the 16 lanes of an A-operand read phase read 16 distinct rows at one
+//     logical chunk; f_k spreads them over the bank groups.
+//  V: a transposed-read phase reads 4 consecutive rows x 64 bytes; f_v puts
+//     the 4 rows in different 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz_split_k(int row) {
+  if constexpr (D == 128) return (row & 7) | ((row >> 1) & 8);
+  else return ((row >> 1) & 3) | ((row >> 2) & 4);
+}
 template <int D>
 __device__ __forceinline__ int swz_split_v(int row) {
   if constexpr (D == 128) return (row & 3) << 2;
@@ -68,8 +76,8 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Opart, float* __restrict__ Lpart,
     int H_q, int H_kv, int N_q, int N_kv, int S, int keys_per_split, float c) {
   using C = SplitCfg<D>;
-  // per wave: one V tile; reused at the end for the merge of the 4 waves
-  constexpr int kVBytes = kSplitWaves * C::TILE_BYTES;
+  // per wave: one K and one V tile; reused at the end for the merge of the 4 waves
+  constexpr int kVBytes = kSplitWaves * 2 * C::TILE_BYTES;
   constexpr int kMergeBytes = kSplitWaves * D * 32 * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
   __shared__ float ms[kSplitWaves][32], ls[kSplitWaves][32];
@@ -111,7 +119,8 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
   const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
   const uint16_t* Kh = K + kvbase;
   const uint8_t* Vh = reinterpret_cast<const uint8_t*>(V + kvbase);
-  uint8_t* vt = lds + wave * C::TILE_BYTES;
+  uint8_t* kt = lds + wave * 2 * C::TILE_BYTES;
+  uint8_t* vt = kt + C::TILE_BYTES;
 
   // transposed-read offsets of V (as in the main forward kernel)
   const int j16 = lane & 15;
@@ -123,7 +132,13 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
     const int cc = 32 * sb + 16 * vgrp + 4 * (j16 & 3);
     voff[sb] = row * C::ROW_BYTES + (((cc >> 3) ^ swz_split_v<D>(row)) * 16) + (cc & 7) * 2;
   }
+  // K A-operand reads: row row_of_lane(col) (accumulator register i of lane
+  // half g then holds key 16g + i), logical chunk (D/16)*half + t
   const int krow_lane = row_of_lane(col);
+  int koff[C::KST];
+#pragma unroll
+  for (int t = 0; t < C::KST; ++t)
+    koff[t] = krow_lane * C::ROW_BYTES + ((((D / 16) * half + t) ^ swz_split_k<D>(krow_lane)) * 16);
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -133,29 +148,25 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
 
   for (int tt = wave; tt < ntiles; tt += kSplitWaves) {
     const int k0 = kb + tt * kSplitBK;
-    // K rows as the A operand (rows permuted so that accumulator register i of
-    // lane half g holds key 16g + i); rows past the end repeat the last key
-    bf16x8 ka[C::KST];
-    {
-      const uint16_t* kp = Kh + size_t(min(k0 + krow_lane, N_kv - 1)) * D + half * (D / 2);
-#pragma unroll
-      for (int t = 0; t < C::KST; ++t) ka[t] = as_bf16x8(ld_global16(kp + 8 * t));
-    }
-    // V tile into this wave's LDS buffer (swizzled 16-byte chunks)
+    // K and V tiles into this wave's LDS buffers by LDS-DMA (each instruction
+    // moves 1 KiB of consecutive rows; swizzled 16-byte chunks); rows past the
+    // end repeat the last key
 #pragma unroll
     for (int ig = 0; ig < C::NDMA; ++ig) {
       const int row = C::RPI * ig + lane / C::CPR;
       const int pch = lane % C::CPR;
-      const int grow = min(k0 + row, N_kv - 1);
-      lds_dma16(Vh + size_t(grow) * C::ROW_BYTES + ((pch ^ swz_split_v<D>(row)) * 16),
-                (LDS_AS void*)(vt + 1024 * ig));
+      const size_t grow = size_t(min(k0 + row, N_kv - 1)) * C::ROW_BYTES;
+      lds_dma16(reinterpret_cast<const uint8_t*>(Kh) + grow + ((pch ^ swz_split_k<D>(row)) * 16),
+                (LDS_AS void*)(kt + 1024 * ig));
+      lds_dma16(Vh + grow + ((pch ^ swz_split_v<D>(row)) * 16), (LDS_AS void*)(vt + 1024 * ig));
     }
     wait_vmem();
 
-    // S^T = K Q^T (keys x rows; lane = row)
+    // S^T = K Q^T (keys x rows; lane = row), K rows read from LDS
     f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int t = 0; t < C::KST; ++t) sacc = mfma32x32x16(ka[t], qreg[t], sacc);
+    for (int t = 0; t < C::KST; ++t)
+      sacc = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[t])), qreg[t], sacc);
     // key k0 + 16*half + i is visible iff i <= lim
     const int lim = last_key - k0 - 16 * half;
 #pragma unroll
