@@ -1,0 +1,90 @@
+"""The largest sizes the ABI accepts, on closed forms built on the device
+(no host-side data): with Q = 0 every allowed key has weight 1/count, so
+O_i is the mean of the allowed V rows and LSE_i = ln(count). V row j is the
+one-hot vector e_(j mod d), so the mean is count(j in allowed, j = c mod d)
+/ count for column c, exactly. This exercises 64-bit offsets of K/V rows
+past 2^31 bytes (N_kv = 2^24 keys of 256 bytes)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import ensure_library, o_within, to_f64
+from workloads import DTYPE_BF16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_library()
+
+
+def one_hot_v(H_kv, n, d):
+    import torch
+    v = torch.zeros((1, H_kv, n, d), dtype=torch.bfloat16, device="cuda")
+    idx = torch.arange(n, device="cuda") % d
+    v[0, :, torch.arange(n, device="cuda"), idx] = 1.0
+    return v
+
+
+def expected(rows, n_allowed_of, d):
+    """O[r, c] = #{j < n_allowed(r) : j = c mod d} / n_allowed(r)."""
+    out = np.zeros((len(rows), d))
+    for a, i in enumerate(rows):
+        n = n_allowed_of(i)
+        base, rem = divmod(n, d)
+        out[a] = base + (np.arange(d) < rem)
+        out[a] /= n
+    return out
+
+
+def test_noncausal_forward_2p24_keys():
+    import exact_attention_109_amd as fa
+    import torch
+    n_kv, n_q, d = 1 << 24, 256, 128
+    q = torch.zeros((1, 1, n_q, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 1, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    v = one_hot_v(1, n_kv, d)
+    o, lse = fa.fwd(q, k, v)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 255]
+    ref = expected(rows, lambda i: n_kv, d)
+    assert o_within(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
+    assert np.all(np.abs(to_f64(lse)[0, 0] - math.log(n_kv)) <= 1e-3)
+    del k, v
+
+
+def test_splitkv_decode_2p24_keys():
+    import exact_attention_109_amd as fa
+    import torch
+    n_kv, d = 1 << 24, 128
+    q = torch.zeros((1, 4, 1, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 1, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    v = one_hot_v(1, n_kv, d)
+    o, lse = fa.fwd_splitkv(q, k, v, 64)
+    torch.cuda.synchronize()
+    ref = expected([0], lambda i: n_kv, d)
+    for h in range(4):
+        assert o_within(to_f64(o)[0, h, [0]], ref, DTYPE_BF16)
+    assert np.all(np.abs(to_f64(lse) - math.log(n_kv)) <= 1e-3)
+    del k, v
+
+
+def test_causal_forward_2p20():
+    import exact_attention_109_amd as fa
+    import torch
+    n, d = 1 << 20, 128
+    q = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device="cuda")
+    v = one_hot_v(1, n, d)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2, 127, 128, 65535, 65536, n - 257, n - 1]
+    ref = expected(rows, lambda i: i + 1, d)
+    assert o_within(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
+    got = to_f64(lse)[0, 0, rows]
+    assert np.all(np.abs(got - np.log(np.array(rows) + 1.0)) <= 1e-3)
