@@ -11,6 +11,8 @@ Contents:
   attention  -- materialized forward (O, LSE) and textbook backward
   blockwise  -- the Q-stationary blockwise (m, d, O) update, a second route
   bruteforce -- scalar Python loops for tiny shapes, a third route
+  fp8        -- e4m3 codes, the 128-row block quantizer (float32 recipe),
+                dequantization and the forward on dequantized inputs
 
 Every function is pinned by CPU tests against values and identities the
 source pages and the mathematics fix (see tests/test_oracle.py); none is
