@@ -31,6 +31,7 @@ from workloads import (DECODE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, cu_seqlens
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: twice the bf16 rate
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_fa_fwd.json")
 
@@ -239,6 +240,70 @@ def time_varlen(fa, torch, steps: int):
     }
 
 
+def time_fp8(fa, torch, steps: int):
+    """FP8 forward on the bench configuration: the bf16 inputs are block-
+    quantized on the GPU (fa_quantize_fp8, q and k row-major, v d-major), then
+    fa_fwd_fp8 is timed. Throughput against the dense-fp8 MFMA peak; the
+    output's deviation from the bf16 forward on the unquantized inputs is
+    reported beside it (relative RMS and max |dO| over all elements, max
+    |dLSE|)."""
+    w = WORKLOADS["c3"]
+    inp = make_inputs(w)
+    q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+    stream = torch.cuda.current_stream()
+    # quantizer: one pass over the three tensors (bf16 in, codes + scales out)
+    fa.quantize_fp8(q)
+    torch.cuda.synchronize()
+    qa = torch.cuda.Event(enable_timing=True)
+    qb = torch.cuda.Event(enable_timing=True)
+    qa.record(stream)
+    q8, qd = fa.quantize_fp8(q)
+    k8, kd = fa.quantize_fp8(k)
+    v8, vd = fa.quantize_fp8(v, d_major=True)
+    qb.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = qa.elapsed_time(qb)
+    qbytes = 3 * (q.numel() * 3) + 4 * (qd.numel() + kd.numel() + vd.numel())
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
+    t0 = time.perf_counter()
+    n = 0
+    while n < 5 or time.perf_counter() - t0 < 1.0:
+        fa.fwd_fp8(q8, qd, k8, kd, v8, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in per:
+        a.record(stream)
+        fa.fwd_fp8(q8, qd, k8, kd, v8, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in per]
+    avg = float(np.mean(ms))
+    tf = w.fwd_flop / (avg * 1e-3) / 1e12
+    o_ref, lse_ref = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    diff = o.float() - o_ref.float()
+    rel_rms = float(diff.square().mean().sqrt() / o_ref.float().square().mean().sqrt())
+    return {
+        "workload": w.name + "_fp8",
+        "entry_point": "fa_fwd_fp8",
+        "dtype": "e4m3 inputs (128-row block scales), f32 scores, e4m3 P, bf16 O",
+        "avg_launch_ms": round(avg, 4),
+        "median_launch_ms": round(float(np.median(ms)), 4),
+        "min_launch_ms": round(float(np.min(ms)), 4),
+        "tflops": round(tf, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "kernel": "fwd_fp8_kernel"},
+        "vs_bf16_path": {"o_rel_rms": round(rel_rms, 6), "o_max_abs": round(float(diff.abs().max()), 5),
+                         "lse_max_abs": round(float((lse - lse_ref).abs().max()), 5)},
+        "quantize": {"ms_three_tensors": round(quant_ms, 4), "bytes": qbytes,
+                     "gbs": round(qbytes / (quant_ms * 1e-3) / 1e9, 1)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +317,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement on c5")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
@@ -368,6 +434,9 @@ def main():
     if not args.no_varlen:
         print("# timing the packed variable-length forward", file=sys.stderr, flush=True)
         result["varlen"] = time_varlen(fa, torch, max(5, args.steps // 2))
+    if not args.no_fp8:
+        print("# timing the FP8 forward", file=sys.stderr, flush=True)
+        result["fp8"] = time_fp8(fa, torch, max(5, args.steps))
     if not args.no_decode:
         print("# timing the split-KV forward on the decode workload", file=sys.stderr, flush=True)
         result["decode"] = time_decode(fa, torch, max(5, args.steps))

@@ -2,7 +2,7 @@
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
 fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
-fa_fwd_varlen, fa_fwd_check and fa_status_string. This module exposes the same names with the same
+fa_fwd_varlen, fa_fwd_check, fa_quantize_fp8, fa_fwd_fp8 and fa_status_string. This module exposes the same names with the same
 arguments (device pointers as integers, sizes, flags, a stream handle) plus
 convenience wrappers over torch tensors:
 
@@ -10,6 +10,8 @@ convenience wrappers over torch tensors:
     o, lse = fwd_splitkv(q, k, v, num_splits, causal=False, scale=None)
     o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, scale=None)
     err = fwd_check(q, k, lse, rows, causal=False, scale=None)
+    codes, descale = quantize_fp8(x, d_major=False)
+    o, lse = fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
 
 The wrappers only marshal arguments: torch allocates device memory and
@@ -67,6 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_check.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, vp]
     lib.fa_fwd_check.restype = i
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.fa_quantize_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -111,6 +117,16 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q
 def fa_fwd_check(q, k, lse, rows, n_rows, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, result, stream) -> int:
     return load_library().fa_fwd_check(q, k, lse, rows, n_rows, B, H_q, H_kv, N_q, N_kv, d, int(causal),
                                        float(scale), dtype, result, stream)
+
+
+def fa_quantize_fp8(x, codes, descale, B, H, N, d, d_major, dtype, stream) -> int:
+    return load_library().fa_quantize_fp8(x, codes, descale, B, H, N, d, int(d_major), dtype, stream)
+
+
+def fa_fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale,
+               stream) -> int:
+    return load_library().fa_fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv,
+                                     d, int(causal), float(scale), stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -297,3 +313,65 @@ __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fw
            "fa_fwd_varlen", "fa_fwd_check", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "fwd_check", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
            "FA_DTYPE_BF16", "LIB_PATH"]
+
+
+FP8_BLOCK = 128   # rows per descale block
+
+
+def fp8_v_pad(n: int) -> int:
+    """Key count of the d-major FP8 V layout: n rounded up to 128."""
+    return (n + 127) // 128 * 128
+
+
+def quantize_fp8(x, d_major: bool = False, codes=None, descale=None):
+    """Block-quantize a bf16 tensor x [B, H, N, d] to e4m3 codes (uint8).
+
+    Returns (codes, descale): codes [B, H, N, d], or [B, H, d, fp8_v_pad(N)]
+    when d_major (the V layout of fwd_fp8); descale float32 [B, H, ceil(N/128)]."""
+    import torch
+    _check(x, "x", torch.bfloat16)
+    B, H, N, d = x.shape
+    cshape = (B, H, d, fp8_v_pad(N)) if d_major else (B, H, N, d)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty((B, H, (N + FP8_BLOCK - 1) // FP8_BLOCK), dtype=torch.float32, device=x.device)
+    _check(codes, "codes", torch.uint8, cshape)
+    _check(descale, "descale", torch.float32, (B, H, (N + FP8_BLOCK - 1) // FP8_BLOCK))
+    st = fa_quantize_fp8(x.data_ptr(), codes.data_ptr(), descale.data_ptr(), B, H, N, d, d_major,
+                         FA_DTYPE_BF16, _stream_handle(x))
+    if st != FA_OK:
+        raise FaError(st, "fa_quantize_fp8")
+    return codes, descale
+
+
+def fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal: bool = False, scale: float | None = None,
+            out=None, lse=None):
+    """Attention forward on FP8 codes: q8 [B,H_q,N_q,d], k8 [B,H_kv,N_kv,d]
+    (row-major), v8 [B,H_kv,d,fp8_v_pad(N_kv)] (d-major), descales per 128-row
+    block. Returns (o bf16 [B,H_q,N_q,d], lse float32 [B,H_q,N_q])."""
+    import torch
+    B, H_q, N_q, d = q8.shape
+    _, H_kv, N_kv, _ = k8.shape
+    _check(q8, "q8", torch.uint8)
+    _check(k8, "k8", torch.uint8, (B, H_kv, N_kv, d))
+    _check(v8, "v8", torch.uint8, (B, H_kv, d, fp8_v_pad(N_kv)))
+    nbq = (N_q + FP8_BLOCK - 1) // FP8_BLOCK
+    nbk = (N_kv + FP8_BLOCK - 1) // FP8_BLOCK
+    _check(q_descale, "q_descale", torch.float32, (B, H_q, nbq))
+    _check(k_descale, "k_descale", torch.float32, (B, H_kv, nbk))
+    _check(v_descale, "v_descale", torch.float32, (B, H_kv, nbk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H_q, N_q, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q8.device)
+    _check(out, "out", torch.bfloat16, (B, H_q, N_q, d))
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    st = fa_fwd_fp8(q8.data_ptr(), q_descale.data_ptr(), k8.data_ptr(), k_descale.data_ptr(), v8.data_ptr(),
+                    v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H_q, H_kv, N_q, N_kv, d, causal,
+                    scale, _stream_handle(q8))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return out, lse

@@ -288,3 +288,63 @@ FA_EXPORT int fa_fwd_check(const void* q, const void* k, const float* lse, const
   hipError_t err = fa::launch_check(p, rows, n_rows, result, dtype, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+FA_EXPORT int fa_quantize_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int d, int d_major,
+                              int dtype, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (N > kMaxSeq) return FA_ERR_INVALID_ARG;
+  if (!x || !codes || !descale) return FA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(descale)) return FA_ERR_INVALID_ARG;
+  const size_t n_rows = d_major ? size_t(fa::fp8_v_pad(N)) : size_t(N);
+  const size_t x_bytes = size_t(B) * H * N * d * 2;
+  const size_t c_bytes = size_t(B) * H * n_rows * d;
+  const size_t s_bytes = size_t(B) * H * ((N + 127) / 128) * sizeof(float);
+  const Range rx = range_of(x, x_bytes), rc_ = range_of(codes, c_bytes), rs = range_of(descale, s_bytes);
+  if (overlaps(rx, rc_) || overlaps(rx, rs) || overlaps(rc_, rs)) return FA_ERR_INVALID_ARG;
+
+  int rc = check_device();
+  if (rc != FA_OK) return rc;
+  hipError_t err = fa::launch_quantize_fp8(x, codes, descale, B, H, N, d, d_major ? 1 : 0,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_EXPORT int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8, const float* k_descale,
+                         const void* v8, const float* v_descale, void* o, float* lse,
+                         int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, FA_DTYPE_BF16, &empty);
+  if (rc != FA_OK || empty) return rc;
+
+  const size_t q_bytes = size_t(B) * H_q * N_q * d;
+  const size_t k_bytes = size_t(B) * H_kv * N_kv * d;
+  const size_t v_bytes = size_t(B) * H_kv * d * size_t(fa::fp8_v_pad(N_kv));
+  const size_t qs_bytes = size_t(B) * H_q * ((N_q + 127) / 128) * sizeof(float);
+  const size_t ks_bytes = size_t(B) * H_kv * ((N_kv + 127) / 128) * sizeof(float);
+  const size_t o_bytes = size_t(B) * H_q * N_q * d * 2;
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  if (!q8 || !q_descale || !k8 || !k_descale || !v8 || !v_descale || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
+       reinterpret_cast<uintptr_t>(v_descale)) & 3u)
+    return FA_ERR_INVALID_ARG;
+  const Range in[6] = {range_of(q8, q_bytes), range_of(k8, k_bytes), range_of(v8, v_bytes),
+                       range_of(q_descale, qs_bytes), range_of(k_descale, ks_bytes), range_of(v_descale, ks_bytes)};
+  const Range out[2] = {range_of(o, o_bytes), range_of(lse, lse_bytes)};
+  for (const Range& r : out)
+    for (const Range& i : in)
+      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::Fp8FwdParams p{q8, q_descale, k8, k_descale, v8, v_descale, o, lse,
+                     B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipError_t err = fa::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -59,4 +59,26 @@ hipError_t launch_check(const FwdParams& p, const int* rows, int n_rows, float* 
 hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* workspace, hipStream_t stream);
 size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits);
 
+// FP8 forward: e4m3 codes with one float32 descale per 128-row block;
+// v is d-major [B][H_kv][d][fp8_v_pad(N_kv)]; o is bf16, lse float32.
+struct Fp8FwdParams {
+  const void* q;
+  const float* q_descale;
+  const void* k;
+  const float* k_descale;
+  const void* v;
+  const float* v_descale;
+  void* o;
+  float* lse;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+};
+inline int fp8_v_pad(int n) { return (n + 127) / 128 * 128; }
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+// Block quantizer: bf16 x [B][H][N][d] -> codes (row-major, or d-major with
+// zero codes up to fp8_v_pad(N)) and descale [B][H][ceil(N/128)].
+hipError_t launch_quantize_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int d, int d_major,
+                               hipStream_t stream);
+
 }  // namespace fa

@@ -208,6 +208,59 @@ int fa_fwd_check(const void* q, const void* k, const float* lse, const int* rows
                  int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, int dtype,
                  float* result, void* stream);
 
+/*
+ * fa_quantize_fp8 -- block quantization of a bf16 tensor to OCP e4m3 codes.
+ *
+ * FP8 inputs are one of the low-precision paths of the FlashAttention line,
+ * which must handle quantization scales and outliers ("Flash-Attention"
+ * (Awesome System Papers Wiki), key-observation and design-space sections).
+ * x: bf16 [B][H][N][d] (finite values). For every (b, h) and every block of
+ * 128 consecutive rows (the last one may be shorter), in float32:
+ *     amax = max |x| over the block, descale = amax / 448, inv = 448 / amax,
+ *     code = e4m3(x * inv)       round to nearest even, saturated to +-448
+ * (when inv is not finite, i.e. amax = 0 or below 448 / FLT_MAX, every code
+ * of the block is 0). The value a code stands for is e4m3(code) * descale.
+ * Outputs: descale float32 [B][H][ceil(N/128)]; codes uint8, either
+ *   d_major == 0: [B][H][N][d]  (row-major, the layout of q and k for fa_fwd_fp8)
+ *   d_major != 0: [B][H][d][N_pad], N_pad = N rounded up to a multiple of 128,
+ *                 codes past N are 0 (the layout of v for fa_fwd_fp8).
+ * Deterministic and bit-exact (the float32 steps are correctly rounded).
+ * d = 64 or 128, N <= 2^24; B, H or N = 0 is a no-op. Errors: negative
+ * sizes, null or misaligned (16 bytes) pointers, outputs overlapping x or
+ * each other -> FA_ERR_INVALID_ARG; other d or dtype != FA_DTYPE_BF16 ->
+ * FA_ERR_UNSUPPORTED.
+ */
+int fa_quantize_fp8(const void* x, void* codes, float* descale, int B, int H, int N, int d, int d_major,
+                    int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on FP8 (e4m3) inputs with block scales.
+ *
+ * Computes O and LSE as fa_fwd does, for the dequantized inputs
+ *     Q = e4m3(q8) * q_descale,  K = e4m3(k8) * k_descale,  V = e4m3(v8) * v_descale
+ * (descale per 128-row block as written by fa_quantize_fp8), on the FP8
+ * matrix instructions ("深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力"
+ * (rkmt.cn blog), version comparison table: FP8 is one of FlashAttention-3's
+ * additions). The scores and the row sums are float32; the probabilities
+ * are rounded to e4m3 (after multiplication by 64 * vd / vd_max of their V
+ * block) for the P V product only, so one output element is within
+ *     2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |V_j|
+ * of the exact value (w the exact probabilities, L = sum_j exp(s_j - max s),
+ * cv_j = 64 * vd_j / vd_max), plus float32 and bf16 output rounding; the
+ * LSE is as accurate as fa_fwd's in bf16.
+ *   q8 [B][H_q][N_q][d], k8 [B][H_kv][N_kv][d]: row-major codes;
+ *   v8 [B][H_kv][d][N_pad]: d-major codes, N_pad = N_kv rounded up to 128,
+ *       codes past N_kv finite (fa_quantize_fp8 writes 0 there);
+ *   q_descale [B][H_q][ceil(N_q/128)], k_descale and v_descale
+ *       [B][H_kv][ceil(N_kv/128)]: float32, finite and >= 0;
+ *   o: bf16 [B][H_q][N_q][d]; lse: float32 [B][H_q][N_q] (natural log).
+ * d = 64 or 128; causal, GQA, scale and the size limits as fa_fwd. Errors as
+ * fa_fwd (dtype is implied); descale pointers must be 4-byte aligned.
+ */
+int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8, const float* k_descale,
+               const void* v8, const float* v_descale, void* o, float* lse,
+               int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, void* stream);
+
 /* fa_status_string -- a static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

@@ -28,9 +28,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_check", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen",
-                                    "fa_status_string"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_check", "fa_fwd_fp8",
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen",
+                                    "fa_quantize_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -262,3 +262,66 @@ def test_check_invalid_arguments(kw, expect):
 def test_check_noop():
     assert check_call(n_rows=0) == fa.FA_OK
     assert check_call(N_q=0) == fa.FA_OK
+
+
+# ---------------------------------------------------------------------------
+# FP8: block quantizer and forward
+# ---------------------------------------------------------------------------
+
+def quant_call(**kw):
+    x, c, sc = ptrs(3)
+    args = dict(x=x, codes=c, descale=sc, B=2, H=4, N=300, d=128, d_major=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_quantize_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(N=-3), INVALID),
+    (dict(dtype=fa.FA_DTYPE_F32), UNSUP),
+    (dict(d=96), UNSUP),
+    (dict(N=(1 << 24) + 1), INVALID),
+    (dict(x=0), INVALID),
+    (dict(codes=A + STEP + 8), INVALID),        # misaligned
+    (dict(codes=A + 64), INVALID),              # codes inside x
+    (dict(descale=A + STEP + 1024), INVALID),   # descale inside the codes
+])
+def test_quantize_fp8_invalid_arguments(kw, expect):
+    assert quant_call(**kw) == expect
+
+
+def test_quantize_fp8_empty_is_a_noop():
+    assert quant_call(N=0) == fa.FA_OK
+    assert quant_call(B=0, x=0) == fa.FA_OK
+
+
+def fp8_call(**kw):
+    q, qs, k, ks, v, vs, o, lse = ptrs(8)
+    args = dict(q8=q, q_descale=qs, k8=k, k_descale=ks, v8=v, v_descale=vs, o=o, lse=lse, B=1, H_q=8, H_kv=2,
+                N_q=500, N_kv=700, d=128, causal=1, scale=0.088, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(d=80), UNSUP),
+    (dict(H_kv=3), INVALID),
+    (dict(N_kv=0), INVALID),
+    (dict(N_q=(1 << 24) + 1), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=-1.0), UNSUP),
+    (dict(q8=0), INVALID),
+    (dict(v_descale=0), INVALID),
+    (dict(k_descale=A + 3 * STEP + 2), INVALID),   # not 4-byte aligned
+    (dict(v8=A + 4 * STEP + 8), INVALID),          # not 16-byte aligned
+    (dict(o=A + 2 * STEP + 256), INVALID),         # o inside k8
+    (dict(lse=A + 6 * STEP + 512), INVALID),       # lse inside o
+])
+def test_fwd_fp8_invalid_arguments(kw, expect):
+    assert fp8_call(**kw) == expect
+
+
+def test_fwd_fp8_empty_is_a_noop():
+    assert fp8_call(N_q=0) == fa.FA_OK
+    assert fp8_call(B=0) == fa.FA_OK

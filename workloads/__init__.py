@@ -234,3 +234,18 @@ def make_packed_inputs(dtype, H_q, H_kv, total_q, total_k, d, seed) -> Inputs:
     if dtype == DTYPE_BF16:
         arrays = {n: f32_to_bf16_bits(a) for n, a in arrays.items()}
     return Inputs(dtype, arrays)
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs: bf16 sources with a spread of magnitudes between row blocks
+# ---------------------------------------------------------------------------
+
+def block_spread_bits(bits: np.ndarray, seed: int, lo: int, hi: int, block: int = 128) -> np.ndarray:
+    """Multiply every block of ``block`` rows (axis 2) of a bf16 tensor by its
+    own power of two 2^k, k drawn uniformly from [lo, hi] by the seed (exact
+    in bf16 while the values stay in range). Returns new bf16 bits."""
+    B, H, N, d = bits.shape
+    nb = (N + block - 1) // block
+    k = np.random.Generator(np.random.PCG64(seed)).integers(lo, hi + 1, size=(B, H, nb))
+    f = np.repeat(np.exp2(k).astype(np.float32), block, axis=2)[:, :, :N, None]
+    return f32_to_bf16_bits(bf16_bits_to_f32(bits) * f)
