@@ -52,13 +52,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Maximum over all 64 lanes of a wave (every lane gets the result).
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return max_xor32(x);
-}
-
 // exp2 on the VALU transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -76,6 +76,13 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// Maximum over all 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return max_xor32(x);
+}
+
 template <int D>
 struct Fp8Cfg {
   static constexpr int BC = 64;                  // keys per block
