@@ -358,7 +358,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
       }
     }
-    l_run += psum * (1.0f / cv);
+    l_run += psum * __builtin_amdgcn_rcpf(cv);  // v_rcp_f32: 1 ulp
+    // keep the row sum in this phase: left alone, the compiler sinks the
+    // 32 dependent adds past the phase barrier into the next MFMA phase
+    asm volatile("" : "+v"(l_run));
   };
 
   auto no_dma = [](int) __attribute__((always_inline)) {};
