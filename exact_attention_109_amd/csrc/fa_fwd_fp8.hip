@@ -270,9 +270,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   };
+  // The MFMA phase runs at raised wave priority, so that its LDS reads and
+  // MFMAs win issue arbitration against the vector phase of the partner wave
+  // on the same SIMD (the vector phase is the longer one; the matrix core
+  // should not wait for it).
   auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     const bool do_pv = j >= 1;
     const bool do_qk = j < nblk;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_sched_barrier(0);
     if (do_pv) {
       pv_part(vt);
 #pragma unroll
@@ -293,6 +300,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Vector phase of block j: mask, block max, (rare) rescale, exponentials
