@@ -187,6 +187,37 @@ def time_decode(fa, torch, steps: int):
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
+    # the same decode step against an FP8 copy of the cache (quantized on the GPU)
+    k8, kd = fa.quantize_fp8(k)
+    v8, vd = fa.quantize_fp8(v, d_major=True)
+    o8 = torch.empty_like(q)
+    lse8 = torch.empty_like(lse)
+    for _ in range(20):
+        fa.fwd_splitkv_fp8(q, k8, kd, v8, vd, splits, causal=w.causal, scale=w.scale, out=o8, lse=lse8, workspace=ws)
+    torch.cuda.synchronize()
+    per8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a8, b8 in per8:
+        a8.record(stream)
+        fa.fwd_splitkv_fp8(q, k8, kd, v8, vd, splits, causal=w.causal, scale=w.scale, out=o8, lse=lse8, workspace=ws)
+        b8.record(stream)
+    torch.cuda.synchronize()
+    ms8 = [a8.elapsed_time(b8) for a8, b8 in per8]
+    med8 = float(np.median(ms8))
+    nbytes8 = (q.numel() + o.numel()) * 2 + k8.numel() + v8.numel() + 4 * (kd.numel() + vd.numel()) + lse.numel() * 4
+    gbs8 = nbytes8 / (med8 * 1e-3) / 1e9
+    d8 = o8.float() - o.float()
+    fp8_kv = {
+        "entry_point": "fa_fwd_splitkv_fp8",
+        "dtype": "bf16 queries, e4m3 K and V (128-key block scales)",
+        "median_ms": round(med8, 4),
+        "min_ms": round(float(np.min(ms8)), 4),
+        "algorithmic_bytes": nbytes8,
+        "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs8 / 8000.0, 4)},
+        "speedup_vs_bf16_cache": round(med / med8, 3),
+        "vs_bf16_cache": {"o_rel_rms": round(float(d8.square().mean().sqrt() / o.float().square().mean().sqrt()), 5),
+                          "lse_max_abs": round(float((lse8 - lse).abs().max()), 5)},
+    }
     return {
         "workload": w.name,
         "entry_point": "fa_fwd_splitkv",
@@ -198,6 +229,7 @@ def time_decode(fa, torch, steps: int):
                      "frac": round(gbs / 8000.0, 4)},
         "tflops": round(w.fwd_flop / (med * 1e-3) / 1e12, 2),
         "device_copy_gbs": round(copy_gbs, 1),
+        "fp8_kv_cache": fp8_kv,
     }
 
 

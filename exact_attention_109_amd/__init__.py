@@ -2,7 +2,7 @@
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
 fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
-fa_fwd_varlen, fa_fwd_check, fa_quantize_fp8, fa_fwd_fp8 and fa_status_string. This module exposes the same names with the same
+fa_fwd_varlen, fa_fwd_check, fa_quantize_fp8, fa_fwd_fp8, fa_fwd_splitkv_fp8 and fa_status_string. This module exposes the same names with the same
 arguments (device pointers as integers, sizes, flags, a stream handle) plus
 convenience wrappers over torch tensors:
 
@@ -12,6 +12,7 @@ convenience wrappers over torch tensors:
     err = fwd_check(q, k, lse, rows, causal=False, scale=None)
     codes, descale = quantize_fp8(x, d_major=False)
     o, lse = fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal=False, scale=None)
+    o, lse = fwd_splitkv_fp8(q, k8, k_descale, v8, v_descale, num_splits, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
 
 The wrappers only marshal arguments: torch allocates device memory and
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_quantize_fp8.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_splitkv_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -127,6 +130,13 @@ def fa_fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv
                stream) -> int:
     return load_library().fa_fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv,
                                      d, int(causal), float(scale), stream)
+
+
+def fa_fwd_splitkv_fp8(q, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale,
+                       num_splits, workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_fwd_splitkv_fp8(q, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv, d,
+                                             int(causal), float(scale), num_splits, workspace, workspace_bytes,
+                                             stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -374,4 +384,41 @@ def fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal: bool = False, s
                     scale, _stream_handle(q8))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def fwd_splitkv_fp8(q, k8, k_descale, v8, v_descale, num_splits: int | None = None, causal: bool = False,
+                    scale: float | None = None, out=None, lse=None, workspace=None):
+    """Split-KV forward of bf16 queries q [B,H_q,N_q,d] against an FP8 cache:
+    k8 [B,H_kv,N_kv,d] (row-major codes), v8 [B,H_kv,d,fp8_v_pad(N_kv)]
+    (d-major codes), descales per 128-key block ((H_q/H_kv)*N_q <= 32)."""
+    import torch
+    _check(q, "q", torch.bfloat16)
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_kv, _ = k8.shape
+    _check(k8, "k8", torch.uint8, (B, H_kv, N_kv, d))
+    _check(v8, "v8", torch.uint8, (B, H_kv, d, fp8_v_pad(N_kv)))
+    nbk = (N_kv + FP8_BLOCK - 1) // FP8_BLOCK
+    _check(k_descale, "k_descale", torch.float32, (B, H_kv, nbk))
+    _check(v_descale, "v_descale", torch.float32, (B, H_kv, nbk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = default_num_splits(B, H_kv, N_kv, torch.cuda.get_device_properties(q.device).multi_processor_count)
+    if out is None:
+        out = torch.empty((B, H_q, N_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.bfloat16, (B, H_q, N_q, d))
+    _check(lse, "lse", torch.float32, (B, H_q, N_q))
+    need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = fa_fwd_splitkv_fp8(q.data_ptr(), k8.data_ptr(), k_descale.data_ptr(), v8.data_ptr(), v_descale.data_ptr(),
+                            out.data_ptr(), lse.data_ptr(), B, H_q, H_kv, N_q, N_kv, d, causal, scale, num_splits,
+                            ws_ptr, ws_bytes, _stream_handle(q))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv_fp8")
     return out, lse

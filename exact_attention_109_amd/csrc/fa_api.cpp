@@ -348,3 +348,51 @@ FA_EXPORT int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8,
   hipError_t err = fa::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+FA_EXPORT int fa_fwd_splitkv_fp8(const void* q, const void* k8, const float* k_descale, const void* v8,
+                                 const float* v_descale, void* o, float* lse, int B, int H_q, int H_kv, int N_q,
+                                 int N_kv, int d, int causal, float scale, int num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, FA_DTYPE_BF16, &empty);
+  if (rc != FA_OK || empty) return rc;
+
+  const size_t q_bytes = size_t(B) * H_q * N_q * d * 2;
+  const size_t k_bytes = size_t(B) * H_kv * N_kv * d;
+  const size_t v_bytes = size_t(B) * H_kv * d * size_t(fa::fp8_v_pad(N_kv));
+  const size_t s_bytes = size_t(B) * H_kv * ((N_kv + 127) / 128) * sizeof(float);
+  const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
+  if (!q || !k8 || !k_descale || !v8 || !v_descale || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_descale) | reinterpret_cast<uintptr_t>(v_descale)) & 3u)
+    return FA_ERR_INVALID_ARG;
+  const Range in[5] = {range_of(q, q_bytes), range_of(k8, k_bytes), range_of(v8, v_bytes),
+                       range_of(k_descale, s_bytes), range_of(v_descale, s_bytes)};
+  const Range out[2] = {range_of(o, q_bytes), range_of(lse, lse_bytes)};
+  for (const Range& r : out)
+    for (const Range& i : in)
+      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
+
+  if (num_splits < 1 || num_splits > 256) return FA_ERR_INVALID_ARG;
+  if ((H_q / H_kv) * N_q > 32) return FA_ERR_UNSUPPORTED;
+
+  const size_t ws_need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits);
+  if (ws_need > 0) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < ws_need) return FA_ERR_INVALID_ARG;
+    const Range w = range_of(workspace, ws_need);
+    for (const Range& i : in)
+      if (overlaps(w, i)) return FA_ERR_INVALID_ARG;
+    for (const Range& r : out)
+      if (overlaps(w, r)) return FA_ERR_INVALID_ARG;
+  }
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+
+  fa::SplitFp8Params p{q, k8, k_descale, v8, v_descale, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipError_t err = fa::launch_fwd_split_fp8kv(p, num_splits, static_cast<float*>(workspace),
+                                              reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -294,6 +294,292 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
   }
 }
 
+// ---- FP8 key/value cache (e4m3 codes with one scale per 128-key block;
+// V d-major [B][H_kv][D][N_pad]), bf16 queries. The codes are widened to
+// bf16 in registers (exact: every e4m3 value is a bf16 value) and the
+// contractions run on the bf16 MFMA, so the result is the bf16 path's
+// arithmetic on the dequantized K and V: the K block scale multiplies the
+// scores of a tile, the V block scale relative to the head's largest one
+// multiplies P before its bf16 rounding, and the output is multiplied by the
+// largest V scale once. HBM traffic per key: 2 x D bytes instead of 4 x D.
+template <int D>
+struct SplitFp8Cfg {
+  static constexpr int K_TILE = kSplitBK * D;                // 32 keys x D bytes
+  static constexpr int V_TILE = D * kSplitBK;                // D rows x 32 keys
+  static constexpr int K_CPR = D / 16;                       // 16-byte chunks per K row
+  static constexpr int K_RPI = 64 / K_CPR;                   // K rows per 1 KiB DMA instruction
+  static constexpr int K_NDMA = K_TILE / 1024;
+  static constexpr int V_NDMA = V_TILE / 1024;               // 32 d-rows of 32 bytes per instruction
+  static constexpr int KST = D / 16;                         // bf16 MFMA k-steps over d
+  static constexpr int DSUB = D / 32;
+};
+// K rows of D bytes: the 16 lanes of a read phase take rows row_of_lane(0..15)
+// (or 16..31) at one logical chunk.
+template <int D>
+__device__ __forceinline__ int swz_split8_k(int row) {
+  if constexpr (D == 128) return ((row >> 1) & 3) | ((row >> 2) & 4);
+  else return ((row >> 2) & 1) | ((row >> 3) & 2);
+}
+// V^T rows of 32 bytes: a phase reads 16 consecutive rows at one logical chunk.
+__device__ __forceinline__ int swz_split8_v(int row) { return (row >> 3) & 1; }
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 (four dwords), element order kept.
+__device__ __forceinline__ u32x4 widen_fp8x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return r;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
+    const uint16_t* __restrict__ Q, const uint8_t* __restrict__ K, const float* __restrict__ KD,
+    const uint8_t* __restrict__ V, const float* __restrict__ VD, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, float* __restrict__ Opart, float* __restrict__ Lpart, int H_q, int H_kv, int N_q,
+    int N_kv, int n_pad, int S, int keys_per_split, float c0) {
+  using C = SplitFp8Cfg<D>;
+  constexpr int kTileBytes = C::K_TILE + C::V_TILE;
+  constexpr int kVBytes = kSplitWaves * 2 * kTileBytes;  // two tiles per wave: one loading, one in use
+  constexpr int kMergeBytes = kSplitWaves * D * 32 * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+  __shared__ float ms[kSplitWaves][32], ls[kSplitWaves][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int G = H_q / H_kv;
+  const int R = G * N_q;
+
+  const int s = blockIdx.x % S;
+  const int bk = blockIdx.x / S;
+  const int b = bk / H_kv;
+  const int hk = bk % H_kv;
+
+  const int r = min(col, R - 1);
+  const int g = r / N_q;
+  const int qi = r % N_q;
+  const int h = hk * G + g;
+  const size_t qrow_base = ((size_t(b) * H_q + h) * N_q + qi) * D;
+  bf16x8 qreg[C::KST];
+  {
+    const uint16_t* qp = Q + qrow_base + half * (D / 2);
+#pragma unroll
+    for (int t = 0; t < C::KST; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
+  }
+
+  const int kb = s * keys_per_split;
+  int ke = min(N_kv, kb + keys_per_split);
+  if (CAUSAL) ke = min(ke, N_q);
+  const int ntiles = ke > kb ? (ke - kb + kSplitBK - 1) / kSplitBK : 0;
+  const int last_key = min(CAUSAL ? qi : N_kv - 1, ke - 1);
+
+  const size_t kvhead = size_t(b) * H_kv + hk;
+  const uint8_t* Kh = K + kvhead * size_t(N_kv) * D;
+  const uint8_t* Vh = V + kvhead * size_t(D) * n_pad;
+  const int nbk = (N_kv + 127) / 128;
+  const float* kd = KD + kvhead * nbk;
+  const float* vd = VD + kvhead * nbk;
+  // the head's largest V scale (the same in every key range, so that the
+  // partial outputs of all ranges are in the same units)
+  float vmax = 0.f;
+  for (int i = lane; i < nbk; i += 64) vmax = fmaxf(vmax, vd[i]);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o, 64));
+  vmax = fmaxf(max_xor32(vmax), 1.17549435e-38f);
+  const float inv_vmax = 1.0f / vmax;
+
+  uint8_t* buf0 = lds + wave * 2 * kTileBytes;
+  uint8_t* buf1 = buf0 + kTileBytes;
+  // DMA of the tile at key k0 into a buffer: K rows of D bytes (rows past the
+  // end repeat the last key), V^T rows of the 32 keys (inside the padded
+  // rows). Uniform bases plus per-lane 32-bit offsets; the waits are explicit.
+  auto issue_tile = [&](int k0, uint8_t* dst) __attribute__((always_inline)) {
+    const uint32_t kdst = lds_address(dst);
+#pragma unroll
+    for (int ig = 0; ig < C::K_NDMA; ++ig) {
+      const int row = C::K_RPI * ig + lane / C::K_CPR;
+      const int pch = lane % C::K_CPR;
+      const uint32_t off = uint32_t(min(k0 + row, N_kv - 1)) * D + ((pch ^ swz_split8_k<D>(row)) * 16);
+      lds_dma16_sbase_nc(Kh, off, kdst + 1024 * ig);
+    }
+#pragma unroll
+    for (int ig = 0; ig < C::V_NDMA; ++ig) {
+      const int row = 32 * ig + lane / 2;
+      const int pch = lane % 2;
+      const uint32_t off = uint32_t(row) * uint32_t(n_pad) + k0 + ((pch ^ swz_split8_v(row)) * 16);
+      lds_dma16_sbase_nc(Vh, off, kdst + C::K_TILE + 1024 * ig);
+    }
+  };
+
+  // K A-operand: row row_of_lane(col), bytes (D/2)*half + 8t .. +7 for k-step t,
+  // read 16 bytes (two k-steps) at a time
+  const int krow_lane = row_of_lane(col);
+  int koff[C::KST / 2];
+#pragma unroll
+  for (int t2 = 0; t2 < C::KST / 2; ++t2)
+    koff[t2] = krow_lane * D + ((((D / 32) * half + t2) ^ swz_split8_k<D>(krow_lane)) * 16);
+  // V^T A-operand of subtile sb: d row 32 sb + col, keys 16 half .. 16 half + 15
+  int voff[C::DSUB];
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb) {
+    const int row = 32 * sb + col;
+    voff[sb] = row * kSplitBK + ((half ^ swz_split8_v(row)) * 16);
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 oacc[C::DSUB];
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb) oacc[sb] = f32x16{};
+
+  // the query rows and scales are in registers before the first tile DMA, so
+  // that no wait for them inside the loop also waits for a prefetch
+  wait_vmem();
+  if (wave < ntiles) issue_tile(kb + wave * kSplitBK, buf0);
+  int it = 0;
+  for (int tt = wave; tt < ntiles; tt += kSplitWaves, ++it) {
+    const int k0 = kb + tt * kSplitBK;
+    uint8_t* kt = (it & 1) ? buf1 : buf0;
+    uint8_t* vt = kt + C::K_TILE;
+    // the next tile of this wave streams in while this one is used
+    if (tt + kSplitWaves < ntiles) {
+      issue_tile(k0 + kSplitWaves * kSplitBK, (it & 1) ? buf0 : buf1);
+      wait_vmem_keep<C::K_NDMA + C::V_NDMA>();
+    } else {
+      wait_vmem();
+    }
+    const int blk = k0 / 128;
+    const float c = fmaxf(c0 * kd[blk], 1.17549435e-38f);
+    const float rv = vd[blk] * inv_vmax;
+
+    // S^T = K Q^T on bf16 MFMAs, K widened from e4m3
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int t2 = 0; t2 < C::KST / 2; ++t2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(kt + koff[t2]);
+      sacc = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[0], raw[1])), qreg[2 * t2], sacc);
+      sacc = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[2], raw[3])), qreg[2 * t2 + 1], sacc);
+    }
+    const int lim = last_key - k0 - 16 * half;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i > lim) sacc[i] = -INFINITY;
+
+    float mx = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+    const float m_blk = max_xor32(mx) * c;
+    if (__any(m_blk > m_run + kSplitRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[sb][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+
+    u32x4 pk[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(sacc[8 * u + e], c, -m_ref));
+        psum += p[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e] * rv, p[2 * e + 1] * rv);
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T: V^T rows widened from e4m3; one 16-byte read per subtile
+    // holds the keys of both k-steps (16 half + 8u + e)
+#pragma unroll
+    for (int sb = 0; sb < C::DSUB; ++sb) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(vt + voff[sb]);
+      oacc[sb] = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[0], raw[1])), as_bf16x8(pk[0]), oacc[sb]);
+      oacc[sb] = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[2], raw[3])), as_bf16x8(pk[1]), oacc[sb]);
+    }
+  }
+
+  // ---- merge the 4 waves (as in the bf16 kernel); the output is in units of
+  // the largest V scale
+  const float l_tot = sum_xor32(l_run);
+  __syncthreads();
+  float* om = reinterpret_cast<float*>(lds);
+  if (half == 0) {
+    ms[wave][col] = m_run;
+    ls[wave][col] = l_tot;
+  }
+#pragma unroll
+  for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        om[(wave * D + 32 * sb + 8 * a + 4 * half + e) * 32 + col] = oacc[sb][4 * a + e];
+  __syncthreads();
+
+  constexpr int kColsPerThread = D * 32 / kSplitThreads;
+  const int mr = tid % 32;
+  const int d0 = (tid / 32) * kColsPerThread;
+  if (mr < R) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, ms[w][mr]);
+    float wgt[kSplitWaves];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      wgt[w] = M == -INFINITY ? 0.f : fast_exp2(ms[w][mr] - M);
+      L += wgt[w] * ls[w][mr];
+    }
+    const float inv = L > 0.f ? vmax / L : 0.f;
+    float ov[kColsPerThread];
+#pragma unroll
+    for (int j = 0; j < kColsPerThread; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSplitWaves; ++w) acc = fmaf(wgt[w], om[(w * D + d0 + j) * 32 + mr], acc);
+      ov[j] = acc * inv;
+    }
+    const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    const int gg = mr / N_q;
+    const int ii = mr % N_q;
+    const size_t row = (size_t(b) * H_q + hk * G + gg) * N_q + ii;
+    if (S == 1) {
+#pragma unroll
+      for (int j = 0; j < kColsPerThread; j += 4) {
+        u32x2 w2;
+        w2[0] = cvt_pk_bf16(ov[j], ov[j + 1]);
+        w2[1] = cvt_pk_bf16(ov[j + 2], ov[j + 3]);
+        st_global8(O + row * D + d0 + j, w2);
+      }
+      if (d0 == 0) LSE[row] = lse;
+    } else {
+      float* op = Opart + (row * S + s) * D + d0;
+#pragma unroll
+      for (int j = 0; j < kColsPerThread; j += 4) {
+        f32x4 v4;
+        v4[0] = ov[j];
+        v4[1] = ov[j + 1];
+        v4[2] = ov[j + 2];
+        v4[3] = ov[j + 3];
+        *reinterpret_cast<f32x4*>(op + j) = v4;
+      }
+      if (d0 == 0) Lpart[row * S + s] = lse;
+    }
+  }
+}
+
 // Merge of the key ranges of each row, in split order: one workgroup of D
 // threads per row, thread = output column.
 template <int D>
@@ -339,6 +625,24 @@ hipError_t launch(const FwdParams& p, int S, float* ws, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_fp8kv(const SplitFp8Params& p, int S, float* ws, hipStream_t stream) {
+  const int keys_per_split = ((p.N_kv + S - 1) / S + kSplitBK - 1) / kSplitBK * kSplitBK;
+  const long long rows = (long long)p.B * p.H_q * p.N_q;
+  float* Opart = ws;
+  float* Lpart = S > 1 ? ws + rows * S * D : nullptr;
+  const long long nwg = (long long)p.B * p.H_kv * S;
+  hipLaunchKernelGGL((fwd_split_fp8_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream,
+                     static_cast<const uint16_t*>(p.q), static_cast<const uint8_t*>(p.k), p.k_descale,
+                     static_cast<const uint8_t*>(p.v), p.v_descale, static_cast<uint16_t*>(p.o), p.lse, Opart,
+                     Lpart, p.H_q, p.H_kv, p.N_q, p.N_kv, fp8_v_pad(p.N_kv), S, keys_per_split,
+                     p.scale * kLog2e);
+  if (S > 1)
+    hipLaunchKernelGGL((fwd_split_combine_kernel<D>), dim3((unsigned)rows), dim3(D), 0, stream, Opart, Lpart,
+                       static_cast<uint16_t*>(p.o), p.lse, S);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits) {
@@ -352,6 +656,18 @@ hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* work
                     : launch<128, false>(p, num_splits, workspace, stream);
   return p.causal ? launch<64, true>(p, num_splits, workspace, stream)
                   : launch<64, false>(p, num_splits, workspace, stream);
+}
+
+}  // namespace fa
+
+namespace fa {
+
+hipError_t launch_fwd_split_fp8kv(const SplitFp8Params& p, int num_splits, float* workspace, hipStream_t stream) {
+  if (p.d == 128)
+    return p.causal ? launch_fp8kv<128, true>(p, num_splits, workspace, stream)
+                    : launch_fp8kv<128, false>(p, num_splits, workspace, stream);
+  return p.causal ? launch_fp8kv<64, true>(p, num_splits, workspace, stream)
+                  : launch_fp8kv<64, false>(p, num_splits, workspace, stream);
 }
 
 }  // namespace fa

@@ -75,6 +75,22 @@ struct Fp8FwdParams {
   float scale;
 };
 inline int fp8_v_pad(int n) { return (n + 127) / 128 * 128; }
+// Split-KV forward with an FP8 key/value cache: q bf16 [B][H_q][N_q][d],
+// k codes [B][H_kv][N_kv][d], v codes d-major [B][H_kv][d][fp8_v_pad(N_kv)],
+// descales [B][H_kv][ceil(N_kv/128)]; o bf16, lse float32.
+struct SplitFp8Params {
+  const void* q;
+  const void* k;
+  const float* k_descale;
+  const void* v;
+  const float* v_descale;
+  void* o;
+  float* lse;
+  int B, H_q, H_kv, N_q, N_kv, d;
+  int causal;
+  float scale;
+};
+hipError_t launch_fwd_split_fp8kv(const SplitFp8Params& p, int num_splits, float* workspace, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 // Block quantizer: bf16 x [B][H][N][d] -> codes (row-major, or d-major with
 // zero codes up to fp8_v_pad(N)) and descale [B][H][ceil(N/128)].

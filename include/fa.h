@@ -261,6 +261,33 @@ int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8, const flo
                const void* v8, const float* v_descale, void* o, float* lse,
                int B, int H_q, int H_kv, int N_q, int N_kv, int d, int causal, float scale, void* stream);
 
+/*
+ * fa_fwd_splitkv_fp8 -- split-KV forward (as fa_fwd_splitkv) with the keys and
+ * values in FP8: a bf16 query against an e4m3 key/value cache.
+ *
+ * Computes O and LSE for q (bf16 values) and the dequantized
+ *     K = e4m3(k8) * k_descale,  V = e4m3(v8) * v_descale
+ * (one scale per 128-key block, as fa_quantize_fp8 writes them). Decoding
+ * reads every cached key once per new token, so the bytes per key decide its
+ * speed; FP8 halves them (the split-KV idea of the FlashDecoding paragraph of
+ * "深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力" (rkmt.cn blog) §3,
+ * with FP8 inputs, one of FlashAttention-3's additions in that blog's version
+ * table). The codes are widened to bf16 exactly and the arithmetic is
+ * fa_fwd_splitkv's, so the bf16 tolerances of fa_fwd apply against the
+ * exact attention of q and the dequantized K, V.
+ *   q, o: bf16 [B][H_q][N_q][d]; lse float32 [B][H_q][N_q];
+ *   k8: [B][H_kv][N_kv][d] codes; v8: [B][H_kv][d][N_pad] codes, N_pad =
+ *       N_kv rounded up to 128, codes past N_kv finite;
+ *   k_descale, v_descale: float32 [B][H_kv][ceil(N_kv/128)], finite, >= 0.
+ * num_splits, workspace and the (H_q/H_kv)*N_q <= 32 limit as fa_fwd_splitkv
+ * (fa_fwd_splitkv_workspace_size gives the workspace). Errors as
+ * fa_fwd_splitkv; descale pointers must be 4-byte aligned.
+ */
+int fa_fwd_splitkv_fp8(const void* q, const void* k8, const float* k_descale, const void* v8,
+                       const float* v_descale, void* o, float* lse, int B, int H_q, int H_kv, int N_q, int N_kv,
+                       int d, int causal, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* fa_status_string -- a static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);
 

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_check", "fa_fwd_fp8",
-                                    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen",
-                                    "fa_quantize_fp8", "fa_status_string"]
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_workspace_size",
+                                    "fa_fwd_varlen", "fa_quantize_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -325,3 +325,35 @@ def test_fwd_fp8_invalid_arguments(kw, expect):
 def test_fwd_fp8_empty_is_a_noop():
     assert fp8_call(N_q=0) == fa.FA_OK
     assert fp8_call(B=0) == fa.FA_OK
+
+
+def split8_call(**kw):
+    q, k, ks, v, vs, o, lse, ws = ptrs(8)
+    args = dict(q=q, k8=k, k_descale=ks, v8=v, v_descale=vs, o=o, lse=lse, B=2, H_q=8, H_kv=2, N_q=1, N_kv=5000,
+                d=128, causal=0, scale=0.088, num_splits=4, workspace=ws, workspace_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID),
+    (dict(d=96), UNSUP),
+    (dict(H_kv=3), INVALID),
+    (dict(N_kv=0), INVALID),
+    (dict(num_splits=0), INVALID),
+    (dict(num_splits=257), INVALID),
+    (dict(N_q=9), UNSUP),                          # 4 heads x 9 queries > 32 rows
+    (dict(k8=0), INVALID),
+    (dict(v_descale=A + 4 * STEP + 2), INVALID),   # not 4-byte aligned
+    (dict(workspace=0), INVALID),
+    (dict(workspace_bytes=16), INVALID),
+    (dict(o=A + 3 * STEP + 64), INVALID),          # o inside v8
+    (dict(scale=float("inf")), INVALID),
+])
+def test_splitkv_fp8_invalid_arguments(kw, expect):
+    assert split8_call(**kw) == expect
+
+
+def test_splitkv_fp8_empty_is_a_noop():
+    assert split8_call(N_q=0) == fa.FA_OK
+    assert split8_call(B=0) == fa.FA_OK
