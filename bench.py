@@ -189,7 +189,7 @@ def time_decode(fa, torch, steps: int):
     del src, dst
     # the same decode step against an FP8 copy of the cache (quantized on the GPU)
     k8, kd = fa.quantize_fp8(k)
-    v8, vd = fa.quantize_fp8(v, d_major=True)
+    v8, vd = fa.quantize_fp8(v)
     o8 = torch.empty_like(q)
     lse8 = torch.empty_like(lse)
     for _ in range(20):

@@ -390,14 +390,14 @@ def fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal: bool = False, s
 def fwd_splitkv_fp8(q, k8, k_descale, v8, v_descale, num_splits: int | None = None, causal: bool = False,
                     scale: float | None = None, out=None, lse=None, workspace=None):
     """Split-KV forward of bf16 queries q [B,H_q,N_q,d] against an FP8 cache:
-    k8 [B,H_kv,N_kv,d] (row-major codes), v8 [B,H_kv,d,fp8_v_pad(N_kv)]
-    (d-major codes), descales per 128-key block ((H_q/H_kv)*N_q <= 32)."""
+    k8 and v8 [B,H_kv,N_kv,d] (row-major codes), descales per 128-key block
+    ((H_q/H_kv)*N_q <= 32)."""
     import torch
     _check(q, "q", torch.bfloat16)
     B, H_q, N_q, d = q.shape
     _, H_kv, N_kv, _ = k8.shape
     _check(k8, "k8", torch.uint8, (B, H_kv, N_kv, d))
-    _check(v8, "v8", torch.uint8, (B, H_kv, d, fp8_v_pad(N_kv)))
+    _check(v8, "v8", torch.uint8, (B, H_kv, N_kv, d))
     nbk = (N_kv + FP8_BLOCK - 1) // FP8_BLOCK
     _check(k_descale, "k_descale", torch.float32, (B, H_kv, nbk))
     _check(v_descale, "v_descale", torch.float32, (B, H_kv, nbk))

@@ -359,7 +359,7 @@ FA_EXPORT int fa_fwd_splitkv_fp8(const void* q, const void* k8, const float* k_d
 
   const size_t q_bytes = size_t(B) * H_q * N_q * d * 2;
   const size_t k_bytes = size_t(B) * H_kv * N_kv * d;
-  const size_t v_bytes = size_t(B) * H_kv * d * size_t(fa::fp8_v_pad(N_kv));
+  const size_t v_bytes = k_bytes;
   const size_t s_bytes = size_t(B) * H_kv * ((N_kv + 127) / 128) * sizeof(float);
   const size_t lse_bytes = size_t(B) * H_q * N_q * sizeof(float);
   if (!q || !k8 || !k_descale || !v8 || !v_descale || !o || !lse) return FA_ERR_INVALID_ARG;

@@ -294,22 +294,28 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
   }
 }
 
-// ---- FP8 key/value cache (e4m3 codes with one scale per 128-key block;
-// V d-major [B][H_kv][D][N_pad]), bf16 queries. The codes are widened to
-// bf16 in registers (exact: every e4m3 value is a bf16 value) and the
-// contractions run on the bf16 MFMA, so the result is the bf16 path's
-// arithmetic on the dequantized K and V: the K block scale multiplies the
-// scores of a tile, the V block scale relative to the head's largest one
-// multiplies P before its bf16 rounding, and the output is multiplied by the
-// largest V scale once. HBM traffic per key: 2 x D bytes instead of 4 x D.
+// ---- FP8 key/value cache (e4m3 codes with one scale per 128-key block,
+// K and V row-major [B][H_kv][N_kv][D] like a bf16 cache, so that appending a
+// token writes one row), bf16 queries. The codes are widened to bf16 in
+// registers (exact: every e4m3 value is a bf16 value) and the contractions
+// run on the bf16 MFMA, so the result is the bf16 path's arithmetic on the
+// dequantized K and V: the K block scale multiplies the scores of a tile, the
+// V block scale relative to the head's largest one multiplies P before its
+// bf16 rounding, and the output is multiplied by the largest V scale once.
+// HBM traffic per key: 2 x D bytes instead of 4 x D. The V^T operand comes
+// from ds_read_b64_tr_b8: in each 16-lane group, output lane i byte k is byte
+// (i % 8) of the 8 bytes addressed by lane 2k + i/8, so 16 lanes addressing
+// 8 key rows x 16 columns receive 8 consecutive keys of one column each.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct SplitFp8Cfg {
   static constexpr int K_TILE = kSplitBK * D;                // 32 keys x D bytes
-  static constexpr int V_TILE = D * kSplitBK;                // D rows x 32 keys
-  static constexpr int K_CPR = D / 16;                       // 16-byte chunks per K row
-  static constexpr int K_RPI = 64 / K_CPR;                   // K rows per 1 KiB DMA instruction
+  static constexpr int V_TILE = kSplitBK * D;
+  static constexpr int K_CPR = D / 16;                       // 16-byte chunks per row
+  static constexpr int K_RPI = 64 / K_CPR;                   // rows per 1 KiB DMA instruction
   static constexpr int K_NDMA = K_TILE / 1024;
-  static constexpr int V_NDMA = V_TILE / 1024;               // 32 d-rows of 32 bytes per instruction
+  static constexpr int V_NDMA = V_TILE / 1024;
   static constexpr int KST = D / 16;                         // bf16 MFMA k-steps over d
   static constexpr int DSUB = D / 32;
 };
@@ -320,8 +326,13 @@ __device__ __forceinline__ int swz_split8_k(int row) {
   if constexpr (D == 128) return ((row >> 1) & 3) | ((row >> 2) & 4);
   else return ((row >> 2) & 1) | ((row >> 3) & 2);
 }
-// V^T rows of 32 bytes: a phase reads 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int swz_split8_v(int row) { return (row >> 3) & 1; }
+// V rows of D bytes read by ds_read_b64_tr_b8: a 32-lane phase reads 8 key
+// rows x 2 logical chunks; these spread them over all 16 bank groups.
+template <int D>
+__device__ __forceinline__ int swz_split8_v(int row) {
+  if constexpr (D == 128) return ((row >> 1) & 3) << 1;
+  else return ((row >> 2) & 1) << 1;
+}
 
 // 8 e4m3 codes (two dwords) -> 8 bf16 (four dwords), element order kept.
 __device__ __forceinline__ u32x4 widen_fp8x8(uint32_t lo, uint32_t hi) {
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ K, const float* __restrict__ KD,
     const uint8_t* __restrict__ V, const float* __restrict__ VD, uint16_t* __restrict__ O,
     float* __restrict__ LSE, float* __restrict__ Opart, float* __restrict__ Lpart, int H_q, int H_kv, int N_q,
-    int N_kv, int n_pad, int S, int keys_per_split, float c0) {
+    int N_kv, int S, int keys_per_split, float c0) {
   using C = SplitFp8Cfg<D>;
   constexpr int kTileBytes = C::K_TILE + C::V_TILE;
   constexpr int kVBytes = kSplitWaves * 2 * kTileBytes;  // two tiles per wave: one loading, one in use
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
 
   const size_t kvhead = size_t(b) * H_kv + hk;
   const uint8_t* Kh = K + kvhead * size_t(N_kv) * D;
-  const uint8_t* Vh = V + kvhead * size_t(D) * n_pad;
+  const uint8_t* Vh = V + kvhead * size_t(N_kv) * D;
   const int nbk = (N_kv + 127) / 128;
   const float* kd = KD + kvhead * nbk;
   const float* vd = VD + kvhead * nbk;
@@ -394,9 +405,9 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
 
   uint8_t* buf0 = lds + wave * 2 * kTileBytes;
   uint8_t* buf1 = buf0 + kTileBytes;
-  // DMA of the tile at key k0 into a buffer: K rows of D bytes (rows past the
-  // end repeat the last key), V^T rows of the 32 keys (inside the padded
-  // rows). Uniform bases plus per-lane 32-bit offsets; the waits are explicit.
+  // DMA of the tile at key k0 into a buffer: K and V rows of D bytes (rows
+  // past the end repeat the last key). Uniform bases plus per-lane 32-bit
+  // offsets; the waits are explicit.
   auto issue_tile = [&](int k0, uint8_t* dst) __attribute__((always_inline)) {
     const uint32_t kdst = lds_address(dst);
 #pragma unroll
@@ -408,9 +419,9 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
     }
 #pragma unroll
     for (int ig = 0; ig < C::V_NDMA; ++ig) {
-      const int row = 32 * ig + lane / 2;
-      const int pch = lane % 2;
-      const uint32_t off = uint32_t(row) * uint32_t(n_pad) + k0 + ((pch ^ swz_split8_v(row)) * 16);
+      const int row = C::K_RPI * ig + lane / C::K_CPR;
+      const int pch = lane % C::K_CPR;
+      const uint32_t off = uint32_t(min(k0 + row, N_kv - 1)) * D + ((pch ^ swz_split8_v<D>(row)) * 16);
       lds_dma16_sbase_nc(Vh, off, kdst + C::K_TILE + 1024 * ig);
     }
   };
@@ -422,12 +433,21 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
 #pragma unroll
   for (int t2 = 0; t2 < C::KST / 2; ++t2)
     koff[t2] = krow_lane * D + ((((D / 32) * half + t2) ^ swz_split8_k<D>(krow_lane)) * 16);
-  // V^T A-operand of subtile sb: d row 32 sb + col, keys 16 half .. 16 half + 15
-  int voff[C::DSUB];
+  // V^T A-operand of subtile sb, k-step u (keys 16 half + 8u + e): this lane
+  // addresses key row 16 half + 8u + j/2, columns 32 sb + 16 ((lane/16) % 2) + 8 (j % 2)
+  // (j = lane % 16); the transposed read hands each lane 8 keys of its column.
+  int voff[C::DSUB][2];
+  {
+    const int j = lane & 15;
+    const int qh = (lane >> 4) & 1;
 #pragma unroll
-  for (int sb = 0; sb < C::DSUB; ++sb) {
-    const int row = 32 * sb + col;
-    voff[sb] = row * kSplitBK + ((half ^ swz_split8_v(row)) * 16);
+    for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 16 * half + 8 * u + (j >> 1);
+        const int cc = 32 * sb + 16 * qh + 8 * (j & 1);
+        voff[sb][u] = row * D + (((cc >> 4) ^ swz_split8_v<D>(row)) * 16) + (cc & 15);
+      }
   }
 
   float m_run = -INFINITY;
@@ -500,14 +520,16 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_fp8_kernel(
     }
     l_run += psum;
 
-    // O^T += V^T P^T: V^T rows widened from e4m3; one 16-byte read per subtile
-    // holds the keys of both k-steps (16 half + 8u + e)
+    // O^T += V^T P^T: 8 keys of one column per lane by a transposed read,
+    // widened from e4m3
 #pragma unroll
-    for (int sb = 0; sb < C::DSUB; ++sb) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(vt + voff[sb]);
-      oacc[sb] = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[0], raw[1])), as_bf16x8(pk[0]), oacc[sb]);
-      oacc[sb] = mfma32x32x16(as_bf16x8(widen_fp8x8(raw[2], raw[3])), as_bf16x8(pk[1]), oacc[sb]);
-    }
+    for (int sb = 0; sb < C::DSUB; ++sb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(vt + voff[sb][u]));
+        oacc[sb] = mfma32x32x16(as_bf16x8(widen_fp8x8(uint32_t(raw[0]), uint32_t(raw[1]))),
+                                as_bf16x8(pk[u]), oacc[sb]);
+      }
   }
 
   // ---- merge the 4 waves (as in the bf16 kernel); the output is in units of
@@ -635,8 +657,7 @@ hipError_t launch_fp8kv(const SplitFp8Params& p, int S, float* ws, hipStream_t s
   hipLaunchKernelGGL((fwd_split_fp8_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kSplitThreads), 0, stream,
                      static_cast<const uint16_t*>(p.q), static_cast<const uint8_t*>(p.k), p.k_descale,
                      static_cast<const uint8_t*>(p.v), p.v_descale, static_cast<uint16_t*>(p.o), p.lse, Opart,
-                     Lpart, p.H_q, p.H_kv, p.N_q, p.N_kv, fp8_v_pad(p.N_kv), S, keys_per_split,
-                     p.scale * kLog2e);
+                     Lpart, p.H_q, p.H_kv, p.N_q, p.N_kv, S, keys_per_split, p.scale * kLog2e);
   if (S > 1)
     hipLaunchKernelGGL((fwd_split_combine_kernel<D>), dim3((unsigned)rows), dim3(D), 0, stream, Opart, Lpart,
                        static_cast<uint16_t*>(p.o), p.lse, S);

@@ -76,8 +76,8 @@ struct Fp8FwdParams {
 };
 inline int fp8_v_pad(int n) { return (n + 127) / 128 * 128; }
 // Split-KV forward with an FP8 key/value cache: q bf16 [B][H_q][N_q][d],
-// k codes [B][H_kv][N_kv][d], v codes d-major [B][H_kv][d][fp8_v_pad(N_kv)],
-// descales [B][H_kv][ceil(N_kv/128)]; o bf16, lse float32.
+// k and v codes [B][H_kv][N_kv][d], descales [B][H_kv][ceil(N_kv/128)];
+// o bf16, lse float32.
 struct SplitFp8Params {
   const void* q;
   const void* k;

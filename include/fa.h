@@ -276,8 +276,8 @@ int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8, const flo
  * fa_fwd_splitkv's, so the bf16 tolerances of fa_fwd apply against the
  * exact attention of q and the dequantized K, V.
  *   q, o: bf16 [B][H_q][N_q][d]; lse float32 [B][H_q][N_q];
- *   k8: [B][H_kv][N_kv][d] codes; v8: [B][H_kv][d][N_pad] codes, N_pad =
- *       N_kv rounded up to 128, codes past N_kv finite;
+ *   k8, v8: [B][H_kv][N_kv][d] codes, row-major like a bf16 cache (so that
+ *       appending a token writes one row; fa_quantize_fp8 with d_major = 0);
  *   k_descale, v_descale: float32 [B][H_kv][ceil(N_kv/128)], finite, >= 0.
  * num_splits, workspace and the (H_q/H_kv)*N_q <= 32 limit as fa_fwd_splitkv
  * (fa_fwd_splitkv_workspace_size gives the workspace). Errors as

@@ -1,5 +1,6 @@
 """Split-KV forward with an FP8 key/value cache (fa_fwd_splitkv_fp8) on the
-GPU: bf16 queries against e4m3 K and V with 128-key block scales, checked
+GPU: bf16 queries against e4m3 K and V (row-major, as a cache) with 128-key
+block scales, checked
 against the fp64 oracle on q and the dequantized K, V, at the bf16
 path's error bound scaled to the values (the codes are widened to bf16
 exactly, so the arithmetic is the bf16 split-KV path's). The codes come from the oracle's quantizer on the
@@ -38,8 +39,7 @@ def run(inp, k8, kd, v8, vd, causal, scale, S):
     import torch
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q = inp.torch("q", "cuda")
-    o, lse = fa.fwd_splitkv_fp8(q, dev(k8), dev(kd), dev(of8.to_d_major(v8)), dev(vd), S, causal=causal,
-                                scale=scale)
+    o, lse = fa.fwd_splitkv_fp8(q, dev(k8), dev(kd), dev(v8), dev(vd), S, causal=causal, scale=scale)
     torch.cuda.synchronize()
     return to_f64(o), to_f64(lse)
 
