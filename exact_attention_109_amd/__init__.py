@@ -336,8 +336,9 @@ def fp8_v_pad(n: int) -> int:
 def quantize_fp8(x, d_major: bool = False, codes=None, descale=None):
     """Block-quantize a bf16 tensor x [B, H, N, d] to e4m3 codes (uint8).
 
-    Returns (codes, descale): codes [B, H, N, d], or [B, H, d, fp8_v_pad(N)]
-    when d_major (the V layout of fwd_fp8); descale float32 [B, H, ceil(N/128)]."""
+    Returns (codes, descale): codes [B, H, N, d] (the layout fwd_fp8 and
+    fwd_splitkv_fp8 read), or [B, H, d, fp8_v_pad(N)] when d_major;
+    descale float32 [B, H, ceil(N/128)]."""
     import torch
     _check(x, "x", torch.bfloat16)
     B, H, N, d = x.shape
@@ -357,15 +358,15 @@ def quantize_fp8(x, d_major: bool = False, codes=None, descale=None):
 
 def fwd_fp8(q8, q_descale, k8, k_descale, v8, v_descale, causal: bool = False, scale: float | None = None,
             out=None, lse=None):
-    """Attention forward on FP8 codes: q8 [B,H_q,N_q,d], k8 [B,H_kv,N_kv,d]
-    (row-major), v8 [B,H_kv,d,fp8_v_pad(N_kv)] (d-major), descales per 128-row
-    block. Returns (o bf16 [B,H_q,N_q,d], lse float32 [B,H_q,N_q])."""
+    """Attention forward on FP8 codes: q8 [B,H_q,N_q,d], k8 and v8
+    [B,H_kv,N_kv,d] (row-major), descales per 128-row block.
+    Returns (o bf16 [B,H_q,N_q,d], lse float32 [B,H_q,N_q])."""
     import torch
     B, H_q, N_q, d = q8.shape
     _, H_kv, N_kv, _ = k8.shape
     _check(q8, "q8", torch.uint8)
     _check(k8, "k8", torch.uint8, (B, H_kv, N_kv, d))
-    _check(v8, "v8", torch.uint8, (B, H_kv, d, fp8_v_pad(N_kv)))
+    _check(v8, "v8", torch.uint8, (B, H_kv, N_kv, d))
     nbq = (N_q + FP8_BLOCK - 1) // FP8_BLOCK
     nbk = (N_kv + FP8_BLOCK - 1) // FP8_BLOCK
     _check(q_descale, "q_descale", torch.float32, (B, H_q, nbq))

@@ -321,7 +321,7 @@ FA_EXPORT int fa_fwd_fp8(const void* q8, const float* q_descale, const void* k8,
 
   const size_t q_bytes = size_t(B) * H_q * N_q * d;
   const size_t k_bytes = size_t(B) * H_kv * N_kv * d;
-  const size_t v_bytes = size_t(B) * H_kv * d * size_t(fa::fp8_v_pad(N_kv));
+  const size_t v_bytes = k_bytes;
   const size_t qs_bytes = size_t(B) * H_q * ((N_q + 127) / 128) * sizeof(float);
   const size_t ks_bytes = size_t(B) * H_kv * ((N_kv + 127) / 128) * sizeof(float);
   const size_t o_bytes = size_t(B) * H_q * N_q * d * 2;

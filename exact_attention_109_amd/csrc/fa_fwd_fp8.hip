@@ -11,9 +11,8 @@
 // the rkmt.cn blog and of "FlashAttention" (LLM Inference Handbook)).
 //
 // Inputs (codes as produced by fa_quantize_fp8):
-//   q8 [B][H_q][N_q][D], k8 [B][H_kv][N_kv][D]        row-major e4m3 codes
-//   v8 [B][H_kv][D][N_pad]                            d-major, N_pad = N_kv rounded up to 128
-//   *_descale [B][H][ceil(N/128)] float32             value = code * descale of its row block
+//   q8 [B][H_q][N_q][D], k8 and v8 [B][H_kv][N_kv][D]  row-major e4m3 codes
+//   *_descale [B][H][ceil(N/128)] float32              value = code * descale of its row block
 //
 // Arithmetic:
 //  * S^T = K Q^T on the FP8 MFMA (exact products, float32 sums); the block's
@@ -38,8 +37,10 @@
 //    S^T tile n (keys 32n .. 32n+31, A-row permutation row_of_lane) leaves
 //    keys 32n + 16g + i in register i of lane half g, so the 32 P bytes of a
 //    lane half for a 64-key PV step are keys {16g .. 16g+15, 32+16g .. 32+16g+15};
-//  * V d-major: the V^T operand of lane (d row r, half g) is two 16-byte
-//    reads of row r of the V tile (keys 16g.. and 32+16g..), no transposing read.
+//  * V row-major like K (contiguous tile loads): the V^T operand of lane
+//    (d row r, half g) is four ds_read_b64_tr_b8, each handing the lane 8
+//    consecutive keys of its column (in each 16-lane group, output lane i
+//    byte k is byte i % 8 of the 8 bytes addressed by lane 2k + i / 8).
 
 #include <type_traits>
 
@@ -63,6 +64,7 @@ constexpr int kSgVmem = 0x010;
 constexpr int kSgDsRead = 0x100;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // e4m3 x e4m3 -> f32, unit block scales (E8M0 127 = 2^0)
@@ -92,8 +94,6 @@ struct Fp8Cfg {
   static constexpr int PV_STEPS = BC / 64;       // MFMA k-steps over keys
   static constexpr int K_CPR = D / 16;           // 16-byte chunks per K row
   static constexpr int K_RPI = 64 / K_CPR;       // K rows per 1 KiB DMA instruction
-  static constexpr int V_CPR = BC / 16;          // chunks per V^T row
-  static constexpr int V_RPI = 64 / V_CPR;       // V^T rows per DMA instruction
   static constexpr int TILE_BYTES = BC * D;      // K tile and V^T tile
   static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;
 };
@@ -107,14 +107,19 @@ __device__ __forceinline__ int swz_k8(int row) {
   if constexpr (D == 128) return ((row >> 1) & 3) | ((row >> 2) & 4);
   else return ((row >> 2) & 1) | ((row >> 3) & 2);
 }
-//  V^T (rows of 64 bytes): a phase reads 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int swz_v8(int row) { return (row >> 2) & 3; }
+//  V (rows of D bytes) for ds_read_b64_tr_b8: a 32-lane phase reads 8
+//  consecutive key rows x 2 logical chunks.
+template <int D>
+__device__ __forceinline__ int swz_vr8(int row) {
+  if constexpr (D == 128) return ((row >> 1) & 3) << 1;
+  else return ((row >> 2) & 1) << 1;
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const float* __restrict__ QD, const uint8_t* __restrict__ K,
     const float* __restrict__ KD, const uint8_t* __restrict__ V, const float* __restrict__ VD,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv, int n_pad,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_kv,
     int n_qtiles, int xcd_remap, float scale_log2) {
   using C = Fp8Cfg<D>;
   constexpr int BC = C::BC;
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nbq = (N_q + kQuantRows - 1) / kQuantRows;
   const int nbk = (N_kv + kQuantRows - 1) / kQuantRows;
   const uint8_t* __restrict__ Kh = K + kvhead * size_t(N_kv) * D;
-  const uint8_t* __restrict__ Vh = V + kvhead * size_t(D) * n_pad;
+  const uint8_t* __restrict__ Vh = V + kvhead * size_t(N_kv) * D;
   const float* __restrict__ kd = KD + kvhead * nbk;
   const float* __restrict__ vd = VD + kvhead * nbk;
 
@@ -185,30 +190,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
   };
 
-  // ---- LDS-DMA staging by the 4 waves of group B. K tile: BC rows of D
-  // bytes (rows past N_kv read the last key instead); V^T tile: D rows of BC
-  // bytes from the d-major V (the padding up to n_pad keeps every read
-  // inside the row).
+  // ---- LDS-DMA staging by the 4 waves of group B: K and V tiles of BC rows
+  // of D bytes (rows past N_kv read the last key instead), each with its own
+  // chunk swizzle.
   const int tail_blk = (N_kv % BC) ? N_kv / BC : -1;
   const int tail_lim = N_kv - 1 - (N_kv / BC) * BC;
-  uint32_t dma_koff[C::DMA_PER_WAVE], dma_koff_t[C::DMA_PER_WAVE], dma_voff[C::DMA_PER_WAVE];
+  uint32_t dma_koff[C::DMA_PER_WAVE], dma_voff[C::DMA_PER_WAVE], dma_cut[C::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
     const int ig = gw * C::DMA_PER_WAVE + i;
-    const int krow = C::K_RPI * ig + lane / C::K_CPR;
-    const int kp = lane % C::K_CPR;
-    dma_koff[i] = krow * D + (kp ^ swz_k8<D>(krow)) * 16;
-    dma_koff_t[i] = dma_koff[i] - (krow - min(krow, tail_lim)) * D;
-    const int vrow = C::V_RPI * ig + lane / C::V_CPR;
-    const int vp = lane % C::V_CPR;
-    dma_voff[i] = uint32_t(vrow) * uint32_t(n_pad) + (vp ^ swz_v8(vrow)) * 16;
+    const int row = C::K_RPI * ig + lane / C::K_CPR;
+    const int pch = lane % C::K_CPR;
+    dma_koff[i] = row * D + (pch ^ swz_k8<D>(row)) * 16;
+    dma_voff[i] = row * D + (pch ^ swz_vr8<D>(row)) * 16;
+    dma_cut[i] = (row - min(row, tail_lim)) * D;
   }
   auto dma_slot = [&](int i, int jk, int jv, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const bool is_k = i < C::DMA_PER_WAVE;
     const int ii = is_k ? i : i - C::DMA_PER_WAVE;
-    const uint8_t* src = is_k ? Kh + size_t(jk) * BC * D : Vh + size_t(jv) * BC;
+    const int jb = is_k ? jk : jv;
+    const uint8_t* src = (is_k ? Kh : Vh) + size_t(jb) * BC * D;
     uint32_t off = is_k ? dma_koff[ii] : dma_voff[ii];
-    if (is_k && jk == tail_blk) off = dma_koff_t[ii];
+    if (jb == tail_blk) off -= dma_cut[ii];
     lds_dma16_sbase(src, off, lds_address(is_k ? kdst : vdst) + 1024 * (gw * C::DMA_PER_WAVE + ii));
   };
   auto dma_k0 = [&](uint8_t* kdst) __attribute__((always_inline)) {
@@ -224,15 +227,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int t = 0; t < C::QK_STEPS; ++t)
 #pragma unroll
     for (int e = 0; e < 2; ++e) koff[t][e] = krow * D + (((4 * t + 2 * half + e) ^ swz_k8<D>(krow)) * 16);
-  // V^T: row 32s + col, logical chunks half and 2 + half.
-  int voff[C::DSUB][2];
+  // V^T of subtile s: read m (m = 0..3) covers the keys 32 (m/2) + 16 half +
+  // 8 (m%2) + k, k = 0..7; this lane addresses key row (that run's start) +
+  // j/2 and column 32 s + 16 ((lane/16) % 2) + 8 (j % 2), j = lane % 16. The
+  // swizzle depends only on j/2 (runs start at multiples of 8), so the run
+  // start is a constant offset.
+  int voff[C::DSUB];
+  {
+    const int j = lane & 15;
+    const int qh = (lane >> 4) & 1;
+    const int r8 = j >> 1;
 #pragma unroll
-  for (int s = 0; s < C::DSUB; ++s)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int row = 32 * s + col;
-      voff[s][e] = row * BC + (((2 * e + half) ^ swz_v8(row)) * 16);
+    for (int s = 0; s < C::DSUB; ++s) {
+      const int cc = 32 * s + 16 * qh + 8 * (j & 1);
+      voff[s] = (16 * half + r8) * D + (((cc >> 4) ^ swz_vr8<D>(r8)) * 16) + (cc & 15);
     }
+  }
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -247,10 +257,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int u = 0; u < C::PV_STEPS; ++u) {
 #pragma unroll
       for (int s = 0; s < C::DSUB; ++s) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(vt + voff[s][0] + 64 * u);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(vt + voff[s][1] + 64 * u);
-        const i32x8 a = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
-                              int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        i32x2 r[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          r[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (LDS_AS i32x2*)(vt + voff[s] + (64 * u + 32 * (m >> 1) + 8 * (m & 1)) * D));
+        const i32x8 a = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
         oacc[s] = mfma_fp8(a, pk[u], oacc[s]);
       }
     }
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (do_pv) {
       pv_part(vt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
 #pragma unroll
       for (int i = 0; i < C::PV_STEPS * C::DSUB; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -530,7 +542,7 @@ hipError_t launch(const Fp8FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
                      static_cast<const uint8_t*>(p.q), p.q_descale, static_cast<const uint8_t*>(p.k), p.k_descale,
                      static_cast<const uint8_t*>(p.v), p.v_descale, static_cast<uint16_t*>(p.o), p.lse, p.H_q,
-                     p.H_kv, p.N_q, p.N_kv, fp8_v_pad(p.N_kv), n_qtiles, xcd_remap, p.scale * kLog2e);
+                     p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, p.scale * kLog2e);
   return hipGetLastError();
 }
 

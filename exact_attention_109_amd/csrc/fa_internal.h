@@ -59,8 +59,8 @@ hipError_t launch_check(const FwdParams& p, const int* rows, int n_rows, float* 
 hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* workspace, hipStream_t stream);
 size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits);
 
-// FP8 forward: e4m3 codes with one float32 descale per 128-row block;
-// v is d-major [B][H_kv][d][fp8_v_pad(N_kv)]; o is bf16, lse float32.
+// FP8 forward: e4m3 codes with one float32 descale per 128-row block, all
+// row-major; o is bf16, lse float32.
 struct Fp8FwdParams {
   const void* q;
   const float* q_descale;

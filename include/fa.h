@@ -221,9 +221,11 @@ int fa_fwd_check(const void* q, const void* k, const float* lse, const int* rows
  * (when inv is not finite, i.e. amax = 0 or below 448 / FLT_MAX, every code
  * of the block is 0). The value a code stands for is e4m3(code) * descale.
  * Outputs: descale float32 [B][H][ceil(N/128)]; codes uint8, either
- *   d_major == 0: [B][H][N][d]  (row-major, the layout of q and k for fa_fwd_fp8)
+ *   d_major == 0: [B][H][N][d]  (row-major: the layout fa_fwd_fp8 and
+ *                 fa_fwd_splitkv_fp8 read for q, k and v)
  *   d_major != 0: [B][H][d][N_pad], N_pad = N rounded up to a multiple of 128,
- *                 codes past N are 0 (the layout of v for fa_fwd_fp8).
+ *                 codes past N are 0 (key index contiguous, for consumers that
+ *                 want the transposed layout).
  * Deterministic and bit-exact (the float32 steps are correctly rounded).
  * d = 64 or 128, N <= 2^24; B, H or N = 0 is a no-op. Errors: negative
  * sizes, null or misaligned (16 bytes) pointers, outputs overlapping x or
@@ -248,9 +250,8 @@ int fa_quantize_fp8(const void* x, void* codes, float* descale, int B, int H, in
  * of the exact value (w the exact probabilities, L = sum_j exp(s_j - max s),
  * cv_j = 64 * vd_j / vd_max), plus float32 and bf16 output rounding; the
  * LSE is as accurate as fa_fwd's in bf16.
- *   q8 [B][H_q][N_q][d], k8 [B][H_kv][N_kv][d]: row-major codes;
- *   v8 [B][H_kv][d][N_pad]: d-major codes, N_pad = N_kv rounded up to 128,
- *       codes past N_kv finite (fa_quantize_fp8 writes 0 there);
+ *   q8 [B][H_q][N_q][d], k8 and v8 [B][H_kv][N_kv][d]: row-major codes
+ *       (fa_quantize_fp8 with d_major = 0);
  *   q_descale [B][H_q][ceil(N_q/128)], k_descale and v_descale
  *       [B][H_kv][ceil(N_kv/128)]: float32, finite and >= 0;
  *   o: bf16 [B][H_q][N_q][d]; lse: float32 [B][H_q][N_q] (natural log).

@@ -27,8 +27,9 @@ Readings (the pages are silent on all of them):
     x * inv, saturated to +-448. When inv is not finite (amax = 0 or below
     448 / FLT_MAX) every code of the block is 0. Dequantized value =
     e4m3 value * descale;
-  * V is stored d-major ([B][H][d][N_pad], N_pad = N rounded up to 128, zero
-    codes in the padding) so that the key index is contiguous;
+  * the FP8 attention paths read Q, K and V row-major ([B][H][N][d], as the
+    bf16 ones); a d-major copy ([B][H][d][N_pad], N_pad = N rounded up to
+    128, zero codes in the padding) is an optional quantizer output;
   * the FP8 forward computes attention on the dequantized Q, K, V; its exact
     value is the float64 forward of those values (``fp8_attention_forward``).
 """

@@ -100,7 +100,7 @@ def make_fp8_case(B, H_q, H_kv, N_q, N_kv, d, seed, spread=(-4, 4), zero_v_block
 def run_fp8(c, causal, scale):
     import exact_attention_109_amd as fa
     o, lse = fa.fwd_fp8(np_to_torch(c["q8"]), np_to_torch(c["qd"]), np_to_torch(c["k8"]), np_to_torch(c["kd"]),
-                        np_to_torch(of8.to_d_major(c["v8"])), np_to_torch(c["vd"]), causal=causal, scale=scale)
+                        np_to_torch(c["v8"]), np_to_torch(c["vd"]), causal=causal, scale=scale)
     return to_f64(o), lse.cpu().numpy().astype(np.float64)
 
 
