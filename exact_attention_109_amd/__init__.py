@@ -329,7 +329,7 @@ FP8_BLOCK = 128   # rows per descale block
 
 
 def fp8_v_pad(n: int) -> int:
-    """Key count of the d-major FP8 V layout: n rounded up to 128."""
+    """Row length of the quantizer's d-major layout: n rounded up to 128."""
     return (n + 127) // 128 * 128
 
 
