@@ -118,7 +118,9 @@ def fp8_bound(c, b, h, G, causal, scale, rows):
     Scores: |ds_ij| <= GAMMA * scale * sum_k |q_ik k_jk| (+ float32), at most
     D_i over the row; the LSE moves by at most D_i and the probabilities by a
     factor within exp(+-2 D_i). Probability rounding (see fa_fwd_fp8):
-    2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |v_j|."""
+    2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |v_j|. The PV sums: GAMMA of
+    the same sum (the rounded probabilities are at most 1 + 2^-4 of the
+    exact ones, hence the factor 1.07)."""
     hk = h // G
     q = of8.dequantize(c["q8"][b:b + 1, h:h + 1], c["qd"][b:b + 1, h:h + 1])[0, 0]
     k = of8.dequantize(c["k8"][b:b + 1, hk:hk + 1], c["kd"][b:b + 1, hk:hk + 1])[0, 0]
@@ -136,7 +138,10 @@ def fp8_bound(c, b, h, G, causal, scale, rows):
     eff = np.maximum(W, 2.0 ** -6 * wmax / cv[None, :])
     grow = np.exp(2.0 * D)
     wv = W @ np.abs(v)
-    o_bound = 2.0 ** -4 * (eff @ np.abs(v)) * grow + (grow - 1.0) * wv + 1e-5 * wv + 1e-6 * np.abs(v).max()
+    # the PV product runs on the same FP8 instruction: GAMMA of the sum of its
+    # |products| (in output units, w_j |v_j| up to the rounding of P)
+    o_bound = (2.0 ** -4 * (eff @ np.abs(v)) * grow + (grow - 1.0) * wv + GAMMA * (eff @ np.abs(v)) * 1.07
+               + 1e-5 * wv + 1e-6 * np.abs(v).max())
     return O, L, o_bound, D[:, 0] + 1e-5
 
 
