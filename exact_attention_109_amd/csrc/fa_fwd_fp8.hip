@@ -176,7 +176,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float vmax = 0.f;
   for (int i = lane; i < nbk; i += 64) vmax = fmaxf(vmax, vd[i]);
   vmax = wave_max(vmax);
-  const float vmax_safe = fmaxf(vmax, 1.17549435e-38f);
+  // (floor 2^-100: keeps 64 / vmax finite when every V block is zero)
+  const float vmax_safe = fmaxf(vmax, 7.88860905e-31f);
   const float inv_vmax = kCvMax / vmax_safe;
 
   const int nblk_all = (N_kv + BC - 1) / BC;

@@ -220,3 +220,17 @@ def test_fwd_fp8_bench_shape_sampled():
         err = np.abs(got_o[b, h, rows] - O)
         assert np.all(err <= tol + bf16_half_ulp(O)), (b, h)
         assert np.all(np.abs(got_l[b, h, rows] - L) <= ltol), (b, h)
+
+
+def test_fwd_fp8_zero_v_gives_zero_output():
+    """V = 0 everywhere (every V scale 0): O is exactly 0 and the LSE is the
+    oracle's (the scores do not depend on V)."""
+    c = make_fp8_case(1, 2, 1, 200, 300, 128, seed=81)
+    c["v8"][:] = 0
+    c["vd"][:] = 0
+    got_o, got_l = run_fp8(c, True, default_scale(128))
+    assert np.all(got_o == 0)
+    rows = np.arange(200)
+    for h in range(2):
+        _, L, _, ltol = fp8_bound(c, 0, h, 2, True, default_scale(128), rows)
+        assert np.all(np.abs(got_l[0, h] - L) <= ltol), h
