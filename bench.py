@@ -73,6 +73,36 @@ def device_clock_khz(torch):
     return None
 
 
+def sample_clock_power():
+    """One read-only amd-smi query of GPU 0 under load: socket power (W) and
+    the gfx clock of each XCD (MHz). None when amd-smi is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        js = json.loads(r.stdout)
+    except Exception:
+        return None
+    g = js[0] if isinstance(js, list) and js else js
+    if isinstance(g, dict) and "gpu_data" in g and g["gpu_data"]:
+        g = g["gpu_data"][0]
+    if not isinstance(g, dict):
+        return None
+    power = g.get("power", {}).get("socket_power", {})
+    clocks = []
+    for key, val in g.get("clock", {}).items():
+        if key.startswith("gfx_") and isinstance(val, dict) and isinstance(val.get("clk"), dict):
+            try:
+                clocks.append(float(val["clk"]["value"]))
+            except (TypeError, ValueError, KeyError):
+                pass
+    if not clocks:
+        return None
+    return {"socket_power_w": power.get("value") if isinstance(power, dict) else None,
+            "gfx_clock_mhz_mean": round(float(np.mean(clocks)), 1),
+            "gfx_clock_mhz_min": min(clocks), "gfx_clock_mhz_max": max(clocks)}
+
+
 def cpu_baseline(w, inp, budget_s: float = 12.0):
     """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
     import oracle
@@ -109,6 +139,44 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
         "os_cpu_count": os.cpu_count(),
         "blas": blas,
     }
+
+
+def time_other_forward(fa, torch, steps: int, main_name: str):
+    """The forward on the other bf16 configurations (inputs resident, outputs
+    preallocated): per-launch HIP-event times on the launch stream, median and
+    minimum, with the roofline fraction against the dense-bf16 MFMA peak."""
+    out = {}
+    for name in ("c2", "c4", "c4x"):
+        if name == main_name or name not in WORKLOADS:
+            continue
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
+        t0 = time.perf_counter()
+        n = 0
+        while n < 5 or time.perf_counter() - t0 < 0.5:
+            fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        med = float(np.median(ms))
+        tf = w.fwd_flop / (med * 1e-3) / 1e12
+        out[name] = {"workload": w.name, "median_launch_ms": round(med, 4),
+                     "min_launch_ms": round(float(np.min(ms)), 4), "tflops": round(tf, 2),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o, lse, inp
+    return out
 
 
 def time_backward(fa, torch, steps: int, warmup: int):
@@ -353,6 +421,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
+    ap.add_argument("--no-other-fwd", action="store_true",
+                    help="skip the forward on the other bf16 configurations (c2, c4, c4x)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
@@ -391,9 +461,21 @@ def main():
     # W untimed warm-up steps, continued until the GPU has been busy for at
     # least --warmup-seconds: clocks ramp up under load, and a few
     # millisecond-long launches would otherwise be timed at idle clocks.
+    # The GPU holds its socket power at the board limit under this load and
+    # lowers the gfx clock to stay there; one amd-smi sample taken during the
+    # warm-up records the clock the timed launches run at.
+    import threading
+    load_sample = {}
+
+    def _sampler():
+        time.sleep(min(1.0, 0.6 * args.warmup_seconds))
+        load_sample["v"] = sample_clock_power()
+
+    sampler = threading.Thread(target=_sampler, daemon=True)
+    sampler.start()
     t_warm = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
+    while n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds or sampler.is_alive():
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
         n_warm += 1
         if n_warm % 16 == 0:
@@ -455,6 +537,12 @@ def main():
             "min_launch_ms": round(float(np.min(launch_ms)), 4),
             "flop_per_launch": w.fwd_flop,
         },
+        "under_load": None if load_sample.get("v") is None else dict(
+            load_sample["v"],
+            # MFMA busy fraction at the clock actually sustained: achieved over
+            # 4096 FLOP/clk/CU x CUs x the mean gfx clock of the 8 XCDs
+            mfma_frac_at_sustained_clock=round(achieved / (4096 * props.multi_processor_count
+                                                           * load_sample["v"]["gfx_clock_mhz_mean"] * 1e6 / 1e12), 4)),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""),
                    "peak_clock_mhz": None if clock_khz is None else clock_khz / 1000,
@@ -463,6 +551,9 @@ def main():
                    round(4096 * props.multi_processor_count * clock_khz * 1e3 / 1e12, 1)},
         "wall_s_timed_region": round(wall, 3),
     }
+    if not args.no_other_fwd:
+        print("# timing the forward on the other bf16 configurations", file=sys.stderr, flush=True)
+        result["fwd_other_configs"] = time_other_forward(fa, torch, max(10, args.steps), w.name.split("_")[0])
     if not args.no_bwd:
         print("# timing the backward on c5", file=sys.stderr, flush=True)
         result["bwd"] = time_backward(fa, torch, max(3, args.steps // 2), 2)
