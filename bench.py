@@ -154,9 +154,18 @@ def time_other_forward(fa, torch, steps: int, main_name: str):
         q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H_q, w.N_q), dtype=torch.float32, device="cuda")
+        import threading
+        load = {}
+
+        def _sampler():
+            time.sleep(1.2)
+            load["v"] = sample_clock_power()
+
+        th = threading.Thread(target=_sampler, daemon=True)
+        th.start()
         t0 = time.perf_counter()
         n = 0
-        while n < 5 or time.perf_counter() - t0 < 0.5:
+        while n < 5 or time.perf_counter() - t0 < 1.3 or th.is_alive():
             fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
             n += 1
             if n % 16 == 0:
@@ -175,6 +184,10 @@ def time_other_forward(fa, torch, steps: int, main_name: str):
         out[name] = {"workload": w.name, "median_launch_ms": round(med, 4),
                      "min_launch_ms": round(float(np.min(ms)), 4), "tflops": round(tf, 2),
                      "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if load.get("v") is not None:
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            out[name]["under_load"] = dict(load["v"], mfma_frac_at_sustained_clock=round(
+                tf / (4096 * cus * load["v"]["gfx_clock_mhz_mean"] * 1e6 / 1e12), 4))
         del q, k, v, o, lse, inp
     return out
 
@@ -468,18 +481,21 @@ def main():
     load_sample = {}
 
     def _sampler():
-        time.sleep(min(1.0, 0.6 * args.warmup_seconds))
+        # after 1.2 s of back-to-back launches (the power reading is averaged)
+        time.sleep(1.2)
         load_sample["v"] = sample_clock_power()
 
     sampler = threading.Thread(target=_sampler, daemon=True)
-    sampler.start()
     t_warm = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds or sampler.is_alive():
+    while (n_warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds
+           or sampler.is_alive() or n_warm <= 16):
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
         n_warm += 1
         if n_warm % 16 == 0:
             torch.cuda.synchronize()
+            if n_warm == 16:
+                sampler.start()
     torch.cuda.synchronize()
     warm_s = time.perf_counter() - t_warm
 
