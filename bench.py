@@ -200,27 +200,43 @@ def time_backward(fa, torch, steps: int, warmup: int):
     q, k, v, do = (inp.torch(n, "cuda") for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     ws = torch.empty((fa.fa_bwd_workspace_size(w.B, w.H_q, w.N_q),), dtype=torch.uint8, device="cuda")
+    import threading
+    load = {}
+
+    def _sampler():
+        time.sleep(1.2)
+        load["v"] = sample_clock_power()
+
+    th = threading.Thread(target=_sampler, daemon=True)
+    th.start()
     t0 = time.perf_counter()
     n = 0
-    while n < warmup or time.perf_counter() - t0 < 1.0:
+    while n < warmup or time.perf_counter() - t0 < 1.3 or th.is_alive():
         fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
         n += 1
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
         fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
-    b.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    return {"workload": w.name, "ms_per_call": round(ms, 4),
+    per_call = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.median(per_call))
+    return {"workload": w.name, "ms_per_call": round(ms, 4), "mean_ms": round(float(np.mean(per_call)), 4),
+            "min_ms": round(float(np.min(per_call)), 4),
             "tflops_2p5x_convention": round(w.bwd_flop / (ms * 1e-3) / 1e12, 2),
             "frac_of_peak": round(w.bwd_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "note": "FLOP = 2.5 x forward FLOP; the kernels issue 3.5 x (S, dP recomputed in both passes)"}
+            "note": "FLOP = 2.5 x forward FLOP; the kernels issue 3.5 x (S, dP recomputed in both passes)",
+            "under_load": None if load.get("v") is None else dict(
+                load["v"],
+                # MFMA work actually issued (3.5 x forward) over the sustained clock's peak
+                mfma_frac_at_sustained_clock=round(
+                    1.4 * w.bwd_flop / (ms * 1e-3) / (4096 * torch.cuda.get_device_properties(0).multi_processor_count
+                                                      * load["v"]["gfx_clock_mhz_mean"] * 1e6), 4))}
 
 
 def time_decode(fa, torch, steps: int):
@@ -572,7 +588,7 @@ def main():
         result["fwd_other_configs"] = time_other_forward(fa, torch, max(10, args.steps), w.name.split("_")[0])
     if not args.no_bwd:
         print("# timing the backward on c5", file=sys.stderr, flush=True)
-        result["bwd"] = time_backward(fa, torch, max(3, args.steps // 2), 2)
+        result["bwd"] = time_backward(fa, torch, max(30, args.steps), 2)
     if not args.no_varlen:
         print("# timing the packed variable-length forward", file=sys.stderr, flush=True)
         result["varlen"] = time_varlen(fa, torch, max(5, args.steps // 2))

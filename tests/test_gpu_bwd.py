@@ -113,3 +113,21 @@ def test_determinism():
     b = fa.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 2, 2, 2112), (1, 4, 2, 2048)])
+def test_noncausal_long_sequences(d, B, Hq, Hkv, N):
+    """Non-causal backward over many streamed query blocks: 33 blocks of 64
+    queries per head (an odd count, which takes the pipeline's tail path) and
+    a GQA case whose dK/dV sum over two query heads of 32 blocks each."""
+    print(f"case d={d} B={B} Hq={Hq} Hkv={Hkv} N={N}", flush=True)
+    inp = make_inputs_shape(DTYPE_BF16, B, Hq, Hkv, N, N, d, seed=700 + d + N, with_grad=True)
+    scale = default_scale(d)
+    dq, dk, dv = run_fwd_bwd(inp, False, scale)
+    gq, gk, gv = oracle.attention_backward(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"), False, scale)
+    errs = (max_abs(dq, gq), max_abs(dk, gk), max_abs(dv, gv))
+    print("max-abs (dq, dk, dv):", errs, flush=True)
+    for got, ref, e in zip((dq, dk, dv), (gq, gk, gv), errs):
+        assert np.all(np.isfinite(got))
+        assert e <= grad_tol(ref, DTYPE_BF16), errs
