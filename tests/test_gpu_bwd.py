@@ -131,3 +131,49 @@ def test_noncausal_long_sequences(d, B, Hq, Hkv, N):
     for got, ref, e in zip((dq, dk, dv), (gq, gk, gv), errs):
         assert np.all(np.isfinite(got))
         assert e <= grad_tol(ref, DTYPE_BF16), errs
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_logits(causal):
+    """Q and K scaled by 8 (exact in bf16) so that scaled scores reach a few
+    hundred and each probability row is nearly one-hot: the gradients stay
+    finite and match the oracle's."""
+    inp = make_inputs_shape(DTYPE_BF16, 1, 4, 2, 640, 640, 128, seed=911 + int(causal), with_grad=True,
+                            qk_multiplier=8.0)
+    scale = default_scale(128)
+    dq, dk, dv = run_fwd_bwd(inp, causal, scale)
+    q, k, v, do = inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do")
+    print("max |scaled score| of head 0:", float(np.abs(q[0, 0] @ k[0, 0].T).max() * scale), flush=True)
+    gq, gk, gv = oracle.attention_backward(q, k, v, do, causal, scale)
+    errs = (max_abs(dq, gq), max_abs(dk, gk), max_abs(dv, gv))
+    print("max-abs (dq, dk, dv):", errs, "max|ref|:", (np.abs(gq).max(), np.abs(gk).max(), np.abs(gv).max()))
+    for got, ref, e in zip((dq, dk, dv), (gq, gk, gv), errs):
+        assert np.all(np.isfinite(got))
+        assert e <= grad_tol(ref, DTYPE_BF16), errs
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_closed_form(causal):
+    """scale = 0: every allowed key has the same probability, so dQ and dK
+    are exactly zero (both carry the factor scale) and dV_j is the sum of
+    dO_i / (number of keys row i sees) over the rows i that see key j."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 300, 64
+    inp = make_inputs_shape(DTYPE_BF16, B, Hq, Hkv, N, N, d, seed=77 + int(causal), with_grad=True)
+    dq, dk, dv = run_fwd_bwd(inp, causal, 0.0)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    do = inp.f64("do")
+    ref = np.zeros((B, Hkv, N, d))
+    bound = np.zeros((B, Hkv, N, d))
+    for h in range(Hq):
+        for i in range(N):
+            cnt = i + 1 if causal else N
+            ref[0, h // (Hq // Hkv), :cnt] += do[0, h, i] / cnt
+            bound[0, h // (Hq // Hkv), :cnt] += np.abs(do[0, h, i]) / cnt
+    err = np.abs(dv - ref)
+    print("dV max-abs against the closed form:", float(err.max()), flush=True)
+    # each P = 1/count is rounded to bf16 (relative error <= 2^-9) before
+    # P^T dO; 1/count itself comes from exp2 in fp32 (a few ulp); the sum of
+    # Hq * N products is accumulated in fp32 ((n - 1) * 2^-24 of sum |terms|)
+    n_terms = Hq * N
+    rel = 2.0 ** -9 + 2.0 ** -20 + n_terms * 2.0 ** -24
+    assert np.all(err <= rel * bound + 1e-6), float((err - rel * bound).max())
