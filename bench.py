@@ -160,6 +160,7 @@ def time_other_forward(fa, torch, steps: int, main_name: str):
         def _sampler():
             time.sleep(1.2)
             load["v"] = sample_clock_power()
+            time.sleep(0.6)  # launches continue a while after the query before timing
 
         th = threading.Thread(target=_sampler, daemon=True)
         th.start()
@@ -206,6 +207,7 @@ def time_backward(fa, torch, steps: int, warmup: int):
     def _sampler():
         time.sleep(1.2)
         load["v"] = sample_clock_power()
+        time.sleep(0.6)  # launches continue a while after the query before timing
 
     th = threading.Thread(target=_sampler, daemon=True)
     th.start()
@@ -500,6 +502,7 @@ def main():
         # after 1.2 s of back-to-back launches (the power reading is averaged)
         time.sleep(1.2)
         load_sample["v"] = sample_clock_power()
+        time.sleep(0.6)  # launches continue a while after the query before timing
 
     sampler = threading.Thread(target=_sampler, daemon=True)
     t_warm = time.perf_counter()

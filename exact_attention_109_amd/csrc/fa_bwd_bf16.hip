@@ -22,10 +22,11 @@
 //  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
 //          owns 32 queries (Q and dO as register operands) while the K/V
 //          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
-//          dQ^T += K^T dS^T with K read transposed. Software-pipelined: the
-//          vector work of block j is issued together with the MFMAs of block
-//          j+1 (S and dP double-buffered), and K/V arrive by LDS-DMA two
-//          blocks ahead through fence-free barriers.
+//          dQ^T += K^T dS^T with K read transposed. Two workgroups share a
+//          compute unit (240 registers per wave, 64 KiB of LDS each), so the
+//          MFMAs of one wave run beside the vector work of the other wave on
+//          its SIMD; K/V of block j+1 arrive by LDS-DMA while block j is
+//          processed.
 // The accumulator layouts are arranged so that P and dS leave the MFMA
 // accumulators already in the k-layout of the next contraction's B operand
 // (see row_of_lane), and every LDS tile uses one XOR swizzle that is free of
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // Shared pieces of the two main kernels
 // ---------------------------------------------------------------------------
-constexpr int kNBuf = 4;  // LDS buffers of streamed blocks: two in use, two loading
+constexpr int kNBuf = 4;  // LDS buffers of the dK/dV kernel's streamed blocks: two in use, two loading
 
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008;
@@ -425,11 +426,14 @@ constexpr int kQueriesPerWg = 128;  // 4 waves x 32 queries
 //   X(j): S^T = K Q^T, dP^T = V dO^T          (MFMA, K/V rows from LDS)
 //   Y(j): P, dS^T = P (dP - D), packed         (VALU)
 //   Z(j): dQ^T += K^T dS^T                     (MFMA, K read transposed)
-// Iteration j runs Y(j) interleaved with X(j+1) (S/dP double-buffered), then
-// Z(j); the LDS-DMA of block j+3 is issued between the vector work (two
-// blocks of lookahead beyond the one X reads).
+// in that order, with the LDS-DMA of block j+1 into the other buffer issued
+// between the vector work of Y(j). Overlap of MFMA and vector work comes from
+// the second workgroup on the compute unit (two waves per SIMD): within one
+// wave the two barely overlap on this hardware, and the software-pipelined
+// form that needs S/dP twice (420 registers, one wave per SIMD) measured
+// 2-3 % slower.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     float* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, float c,
@@ -437,8 +441,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   using C = BwdCfg<D>;
   constexpr int BK = C::BLK;
   constexpr int DPW = C::DMA_PER_WAVE;
-  __shared__ __attribute__((aligned(1024))) uint8_t ks[kNBuf][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs[kNBuf][C::TILE_BYTES];
+  constexpr int kNB = 2;  // two workgroups per CU: 64 KiB of LDS each
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[kNB][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[kNB][C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -467,9 +472,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       qreg[t] = as_bf16x8(ld_global16(Q + off + 8 * t));
       oreg[t] = as_bf16x8(ld_global16(dO + off + 8 * t));
     }
-    // only MFMAs read these: keep them in AGPRs, out of the vector work's way
-#pragma unroll
-    for (int t = 0; t < C::KST; ++t) asm volatile("" : "+a"(qreg[t]), "+a"(oreg[t]));
   }
   const float l2 = L2[rbase + qc];
   const float dl = Dl[rbase + qc];
@@ -509,69 +511,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   f32x16 dq[C::DSUB];
 #pragma unroll
   for (int s = 0; s < C::DSUB; ++s) dq[s] = f32x16{};
-  f32x16 sA[C::NSUB], pA[C::NSUB], sB[C::NSUB], pB[C::NSUB];  // S^T, dP^T of two blocks
-  u32x4 sk[C::STEPS];                                          // dS^T (bf16) of the current block
-
+  f32x16 sA[C::NSUB], pA[C::NSUB];  // S^T, dP^T of the current block
+  u32x4 sk[C::STEPS];                // dS^T (bf16)
   constexpr int NX = 2 * C::KST * C::NSUB;  // MFMAs of X
   constexpr int NZ = C::STEPS * C::DSUB;    // MFMAs of Z
-  // X(j) from buffer bf into (s, p)
-  auto X = [&](int bf, f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
+  auto X = [&](int bf) __attribute__((always_inline)) {
     const uint8_t* kt = ks[bf];
     const uint8_t* vt = vs[bf];
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
-      sx[n] = f32x16{};
-      px[n] = f32x16{};
+      sA[n] = f32x16{};
+      pA[n] = f32x16{};
     }
 #pragma unroll
     for (int t = 0; t < C::KST; ++t) {
 #pragma unroll
       for (int n = 0; n < C::NSUB; ++n) {
         const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
-        sx[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o)), qreg[t], sx[n]);
-        px[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vt + o)), oreg[t], px[n]);
+        sA[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o)), qreg[t], sA[n]);
+        pA[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vt + o)), oreg[t], pA[n]);
       }
     }
+    schedule_mfma_reads<NX - 4, 1, 4>();
   };
-  // Scores of block j past this lane's query (causal) or past N_kv become
-  // -inf, so that P and dS are exactly 0 there.
-  auto mask_scores = [&](int j, f32x16 (&s)[C::NSUB]) __attribute__((always_inline)) {
-    // key j*BK + 32n + 16*half + i is visible iff 32n + i <= lim
-    const int last_key = CAUSAL ? min(query, N_kv - 1) : N_kv - 1;
-    const int lim = last_key - j * BK - 16 * half;
+  auto Y = [&](int j, int jd, int bfd) __attribute__((always_inline)) {
+    const int kv0 = j * BK;
+    if ((CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv)) {
+      const int last_key = CAUSAL ? min(query, N_kv - 1) : N_kv - 1;
+      const int lim = last_key - j * BK - 16 * half;
 #pragma unroll
-    for (int n = 0; n < C::NSUB; ++n)
+      for (int n = 0; n < C::NSUB; ++n)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * n + i > lim) s[n][i] = -INFINITY;
-  };
-  // Y(j) on (s, p) -> sk; with WITH_X also X(j+1) from buffer bfx into
-  // (sx, px) and the DMA of block jd into buffer bfd.
-  auto YX = [&](auto with_x, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], int bfx,
-                f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB], int jd, int bfd) __attribute__((always_inline)) {
-    constexpr bool WITH_X = decltype(with_x)::value;
-    if constexpr (WITH_X) X(bfx, sx, px);
+        for (int i = 0; i < 16; ++i)
+          if (32 * n + i > lim) sA[n][i] = -INFINITY;
+    }
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[n][i], c, -l2));
-        p[n][i] = pv * (p[n][i] - dl);
-        if constexpr (WITH_X) {
-          const int e = 16 * n + i;
-          if (e % 3 == 1 && e / 3 < kSlots) dma_slot(e / 3, jd, bfd);
-        }
+        const float pv = fast_exp2(fmaf(sA[n][i], c, -l2));
+        pA[n][i] = pv * (pA[n][i] - dl);
+        const int e = 16 * n + i;
+        if (e % 3 == 1 && e / 3 < kSlots) dma_slot(e / 3, jd, bfd);
       }
 #pragma unroll
       for (int w = 0; w < 2; ++w)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(p[n][8 * w + 2 * e], p[n][8 * w + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(pA[n][8 * w + 2 * e], pA[n][8 * w + 2 * e + 1]);
     }
-    if constexpr (WITH_X) {
 #pragma unroll
-      for (int e = 32 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
-      // about 4.5 vector instructions per element over the MFMAs of X(j+1)
-    }
+    for (int e = 32 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
   };
   auto Z = [&](int bf) __attribute__((always_inline)) {
     const uint8_t* kt = ks[bf];
@@ -586,52 +575,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     schedule_mfma_reads<NZ - 4, 2, 8>();
   };
-  auto need_mask = [&](int j) __attribute__((always_inline)) {
-    const int kv0 = j * BK;
-    return (CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv);
-  };
-  // iteration j (< nblk - 1): Y(j) on (s, p) with X(j+1) into (sx, px), then Z(j)
-  auto iteration = [&](int j, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], f32x16 (&sx)[C::NSUB],
-                       f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
-    const int jd = min(j + 3, nblk - 1);  // past the end: a harmless reload into a free buffer
-    if (need_mask(j)) mask_scores(j, s);
-    __builtin_amdgcn_sched_barrier(0);
-    YX(std::true_type{}, s, p, (j + 1) % kNBuf, sx, px, jd, (j + 3) % kNBuf);
-    __builtin_amdgcn_sched_barrier(0);
-    Z(j % kNBuf);
-    wait_vmem_keep<kSlots>();  // block j+2 (loaded since the last iteration) is in LDS
-    barrier_nofence();
-  };
-  auto last = [&](int j, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB]) __attribute__((always_inline)) {
-    if (need_mask(j)) mask_scores(j, s);
-    __builtin_amdgcn_sched_barrier(0);
-    YX(std::false_type{}, s, p, 0, sB, pB, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    Z(j % kNBuf);
-  };
 
-  // blocks 0, 1, 2 into buffers 0, 1, 2, X(0), then the pipeline
+  // block 0 into buffer 0; block j+1 is loaded into the other buffer while
+  // block j is processed (the buffer's previous block was finished before
+  // the last barrier)
 #pragma unroll
   for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, 0);
-#pragma unroll
-  for (int i = 0; i < kSlots; ++i) dma_slot(i, min(1, nblk - 1), 1);
-#pragma unroll
-  for (int i = 0; i < kSlots; ++i) dma_slot(i, min(2, nblk - 1), 2);
   wait_vmem();
   __syncthreads();
-  X(0, sA, pA);
-  schedule_mfma_reads<NX - 4, 1, 4>();
-  __builtin_amdgcn_sched_barrier(0);
-  int j = 0;
-  for (; j + 2 < nblk; j += 2) {
-    iteration(j, sA, pA, sB, pB);
-    iteration(j + 1, sB, pB, sA, pA);
-  }
-  if (j + 1 < nblk) {
-    iteration(j, sA, pA, sB, pB);
-    last(j + 1, sB, pB);
-  } else {
-    last(j, sA, pA);
+  for (int j = 0; j < nblk; ++j) {
+    const int bf = j & 1;
+    const int jd = min(j + 1, nblk - 1);  // past the end: a harmless reload
+    X(bf);
+    __builtin_amdgcn_sched_barrier(0);
+    Y(j, jd, bf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    Z(bf);
+    wait_vmem();
+    barrier_nofence();
   }
 
   if (query < N_q) {
