@@ -34,6 +34,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: twice the bf16 rate
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_fa_fwd.json")
+_NO_CLOCK_SAMPLE = False  # set by --no-clock-sample
 
 
 def kernel_source_hash() -> str:
@@ -77,6 +78,12 @@ def sample_clock_power():
     """One read-only amd-smi query of GPU 0 under load: socket power (W) and
     the gfx clock of each XCD (MHz). None when amd-smi is unavailable."""
     import subprocess
+    # Under a profiler (rocprofv3 preloads its library into every child
+    # process, which initialises the GPU there before amd-smi's launcher
+    # replaces itself with python3) the query is skipped.
+    if _NO_CLOCK_SAMPLE or any(key.startswith("ROCPROF") for key in os.environ) \
+            or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     try:
         r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0", "--json"],
                            capture_output=True, text=True, timeout=20)
@@ -452,12 +459,16 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="do not query amd-smi for the clock and power under load")
     ap.add_argument("--no-other-fwd", action="store_true",
                     help="skip the forward on the other bf16 configurations (c2, c4, c4x)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (HBM "
                          "counter calibration for the traffic figure) and exit")
     args = ap.parse_args()
+    global _NO_CLOCK_SAMPLE
+    _NO_CLOCK_SAMPLE = args.no_clock_sample
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path is "
