@@ -414,3 +414,88 @@ def test_pins_reject_planted_mistakes(kind):
 
 def test_pins_reject_wrong_gqa_mapping():
     assert not _pins_pass(oatt.head_forward, gqa_kind="modulo")
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes in the backward: copies of the textbook gradients with one
+# plausible bug each must fail the finite-difference pin or the identities.
+# ---------------------------------------------------------------------------
+
+def _mutant_backward(kind):
+    def backward(q, k, v, do, causal, scale):
+        B, H_q, N_q, d = q.shape
+        H_kv = k.shape[1]
+        G = H_q // H_kv
+        s = oracle.fp32_scale(scale)
+        dq = np.zeros(q.shape)
+        dk = np.zeros(k.shape)
+        dv = np.zeros(v.shape)
+        for b in range(B):
+            for h in range(H_q):
+                hk = h // G
+                qh, kh, vh, doh = q[b, h], k[b, hk], v[b, hk], do[b, h]
+                P = oracle.head_probabilities(qh, kh, causal, scale)
+                dP = doh @ vh.T
+                D = np.sum(P * dP, axis=1, keepdims=True)
+                if kind == "d_from_do_only":
+                    D = np.sum(doh, axis=1, keepdims=True)
+                dS = P * (dP - D)
+                if kind == "no_minus_d":
+                    dS = P * dP
+                gq = s * (dS @ kh)
+                gk = s * (dS.T @ qh)
+                gv = P.T @ doh
+                if kind == "dq_no_scale":
+                    gq = dS @ kh
+                if kind == "dk_uses_do":
+                    gk = s * (dS.T @ doh)
+                if kind == "dv_uses_dp":
+                    gv = dS.T @ doh
+                dq[b, h] = gq
+                if kind == "gqa_overwrite":
+                    dk[b, hk] = gk
+                    dv[b, hk] = gv
+                else:
+                    dk[b, hk] += gk
+                    dv[b, hk] += gv
+        return dq, dk, dv
+    return backward
+
+
+def _backward_pins_pass(backward):
+    """Central differences on a tiny GQA shape (both masks) and the
+    sum identities of dV and dK."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, nq, nkv, d = 1, 2, 1, 4, 5, 3
+    q, k, v = rand_qkv(rng, B, Hq, Hkv, nq, nkv, d)
+    do = rng.standard_normal(q.shape)
+    scale = 0.7
+    ok = True
+    for causal in (False, True):
+        dq, dk, dv = backward(q, k, v, do, causal, scale)
+        for arr, grad in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(arr)
+            it = np.nditer(arr, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                old = arr[idx]
+                arr[idx] = old + 1e-6
+                lp = _loss(q, k, v, do, causal, scale)
+                arr[idx] = old - 1e-6
+                lm = _loss(q, k, v, do, causal, scale)
+                arr[idx] = old
+                num[idx] = (lp - lm) / 2e-6
+            ok &= np.max(np.abs(num - grad)) / max(1.0, np.max(np.abs(grad))) <= 1e-6
+        ok &= np.max(np.abs(dv[0, 0].sum(axis=0) - do[0].sum(axis=(0, 1)))) <= 1e-12
+        ok &= np.max(np.abs(dk[0, 0].sum(axis=0))) <= 1e-12
+    return bool(ok)
+
+
+def test_backward_pins_accept_the_oracle():
+    assert _backward_pins_pass(oracle.attention_backward)
+
+
+@pytest.mark.parametrize("kind", ["no_minus_d", "d_from_do_only", "dq_no_scale", "dk_uses_do", "dv_uses_dp",
+                                  "gqa_overwrite"])
+def test_backward_pins_reject_planted_mistakes(kind):
+    assert not _backward_pins_pass(_mutant_backward(kind))
