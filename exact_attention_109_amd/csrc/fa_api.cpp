@@ -125,10 +125,19 @@ FA_EXPORT int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
   if (rc != FA_OK) return rc;
   if (empty) {
-    // No query rows: dk and dv would be all zero, but with B or H_q zero there
-    // is nothing to write; with N_q zero and keys present the caller gets FA_OK
-    // and no writes, as documented for empty problems.
-    return FA_OK;
+    // No query rows (H_q or N_q zero): no query attends any key, so dk and dv
+    // are zero. They hold B*H_kv*N_kv*d elements, which may be non-zero.
+    if (B == 0 || H_kv == 0 || N_kv == 0) return FA_OK;
+    if (N_kv > kMaxSeq) return FA_ERR_INVALID_ARG;
+    const size_t dkv_bytes = size_t(B) * H_kv * N_kv * d * sizeof(float);
+    if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return FA_ERR_INVALID_ARG;
+    if (overlaps(range_of(dk, dkv_bytes), range_of(dv, dkv_bytes))) return FA_ERR_INVALID_ARG;
+    rc = check_device();
+    if (rc != FA_OK) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = fa::launch_zero_f32x4(dk, dkv_bytes / 16, s);
+    if (err == hipSuccess) err = fa::launch_zero_f32x4(dv, dkv_bytes / 16, s);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
 
   const size_t es = elem_size(dtype);

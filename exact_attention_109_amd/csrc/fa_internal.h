@@ -52,6 +52,8 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_varlen_bf16(const FwdParams& p, const VarlenParams& vl, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+// Zero-fill of n4 float4 elements at p (16-byte aligned).
+hipError_t launch_zero_f32x4(float* p, size_t n4, hipStream_t stream);
 // Self-check of a forward result on sampled rows (see fa_fwd_check).
 hipError_t launch_check(const FwdParams& p, const int* rows, int n_rows, float* out, int dtype, hipStream_t stream);
 // Split-KV forward (bf16, rows per key/value head <= 32); workspace holds

@@ -42,7 +42,8 @@
  *    next synchronization.
  *  - Argument checks happen before any HIP call, in this order: negative
  *    sizes; dtype; d; empty problem (B, H_q or N_q zero -> FA_OK, nothing
- *    launched); H_kv; N_kv; sizes; scale; null and misaligned pointers;
+ *    launched; fa_bwd zero-fills dk and dv then, see there); H_kv; N_kv;
+ *    sizes; scale; null and misaligned pointers;
  *    overlap of an output with an input or another output; workspace. Then
  *    the device is checked (gfx950) and the kernels are launched.
  *  - Results are deterministic: the same inputs give bitwise equal outputs.
@@ -110,6 +111,11 @@ size_t fa_bwd_workspace_size(int B, int H_q, int N_q);
  *
  * Inputs : q, k, v, o, dO (dtype), lse (float32).
  * Outputs: dq, dk, dv (float32), fully written; keys no query may attend get 0.
+ * No query rows (H_q or N_q zero, with B, H_kv and N_kv non-zero): no key is
+ * attended, so dk and dv are filled with zeros on the stream; only dk and dv
+ * are checked (non-null, 16-byte aligned, not overlapping each other) and
+ * written, and N_kv must be at most 2^24. B, H_kv or N_kv zero with no query
+ * rows is a no-op.
  * workspace: device memory of at least fa_bwd_workspace_size(B, H_q, N_q)
  * bytes, 16-byte aligned, not overlapping any other argument.
  */

@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
 import os
 import sys
@@ -13,6 +14,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import exact_attention_109_amd as fa  # noqa: E402
+import oracle  # noqa: E402
 from workloads import DTYPE_BF16, DTYPE_F32, Inputs, bf16_bits_to_f64  # noqa: E402
 
 # Tolerances (max-abs against the fp64 oracle on the same rounded inputs).
@@ -49,17 +51,46 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
 
 
-def o_within(got, ref, dtype) -> bool:
-    """Output check. fp32: max-abs <= 1e-5. bf16: per element
-    |got - ref| <= 1e-2 + half a bf16 ulp of ref -- the output is stored in
-    bf16, and rounding even the exact value to bf16 errs by up to half an ulp
-    (0.0156 once |O| >= 4), so the 1e-2 budget applies to the computation on
-    top of the output format's own rounding."""
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.asarray(a).size else 0.0
+
+
+def o_plain_ok(got, ref, dtype) -> bool:
+    """The stated output bound: max-abs <= 1e-2 (bf16) or 1e-5 (fp32)."""
+    return max_abs(got, ref) <= TOL[dtype]["o"]
+
+
+def o_extreme_ok(got, ref) -> bool:
+    """Output bound of the extreme-logit configuration (|s| in the hundreds,
+    Q and K x 8): per element |got - ref| <= 1e-2 + half a bf16 ulp of ref.
+    There the probabilities are nearly one-hot, so O is close to single value
+    rows and reaches |O| >= 4, where rounding even the exact value to bf16
+    errs by up to 2^-6 = 0.0156 > 1e-2."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    return bool(np.all(np.abs(got - ref) <= TOL[DTYPE_BF16]["o"] + bf16_half_ulp(ref)))
+
+
+def o_small_check(got, ref, dtype):
+    """Output check of the tiny-shape grid. fp32: max-abs <= 1e-5. bf16:
+    max-abs <= 1e-2 on every element whose exact value has |O| < 2. Rows of
+    one to a few keys can hold |O| in [2, 4), where the output's own bf16
+    rounding costs up to 2^-8 = 0.0078 and the bf16 probabilities of the P V
+    product (relative 2^-9 each, not averaged out over so few keys) can add
+    about 0.003 more; those elements are held to 1e-2 + half a bf16 ulp of
+    the exact value. Returns the number of elements that needed that
+    allowance (0 when the plain bound holds everywhere)."""
     got = np.asarray(got)
     ref = np.asarray(ref)
     if dtype == DTYPE_F32:
-        return max_abs(got, ref) <= TOL[DTYPE_F32]["o"]
-    return bool(np.all(np.abs(got - ref) <= TOL[DTYPE_BF16]["o"] + bf16_half_ulp(ref)))
+        assert max_abs(got, ref) <= TOL[DTYPE_F32]["o"]
+        return 0
+    err = np.abs(got - ref)
+    plain = err <= TOL[DTYPE_BF16]["o"]
+    big = np.abs(ref) >= 2.0
+    assert np.all(plain | big), float(err[~big].max())
+    assert np.all(err <= TOL[DTYPE_BF16]["o"] + bf16_half_ulp(ref)), float(err.max())
+    return int(np.count_nonzero(~plain))
 
 
 def sample_rows(n: int, rng: np.random.Generator, count: int = 96, tile: int = 128):
@@ -71,9 +102,47 @@ def sample_rows(n: int, rng: np.random.Generator, count: int = 96, tile: int = 1
     return np.array(sorted(r for r in rows if 0 <= r < n), dtype=np.int64)
 
 
-def max_abs(a, b) -> float:
-    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.asarray(a).size else 0.0
-
-
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def host_workers() -> int:
+    """Threads for running the oracle over independent heads: the host cores
+    this process may use (at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def map_heads(fn, items):
+    """Run fn over independent heads in a thread pool with the BLAS library
+    held to one thread per call (numpy releases the GIL in its matrix
+    products and element-wise kernels). Returns the results in order. This
+    only distributes calls of the oracle; it changes none of its arithmetic."""
+    items = list(items)
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover - threadpoolctl is installed here
+        limiter = None
+    try:
+        with cf.ThreadPoolExecutor(max_workers=host_workers()) as ex:
+            return list(ex.map(fn, items))
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+
+
+def oracle_forward_all(q, k, v, causal, scale, G):
+    """The oracle's O and LSE for every (batch, head), heads run in parallel."""
+    B, H_q = q.shape[0], q.shape[1]
+    heads = [(b, h) for b in range(B) for h in range(H_q)]
+    res = map_heads(lambda bh: oracle.head_forward(q[bh[0], bh[1]], k[bh[0], bh[1] // G], v[bh[0], bh[1] // G],
+                                                   causal, scale), heads)
+    O = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    L = np.empty(q.shape[:3], dtype=np.float64)
+    for (b, h), (o, l) in zip(heads, res):
+        O[b, h], L[b, h] = o, l
+    return O, L

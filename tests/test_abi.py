@@ -117,8 +117,22 @@ def test_empty_problem_is_a_noop():
     assert fwd_call(B=0) == fa.FA_OK
     assert fwd_call(N_q=0) == fa.FA_OK
     assert fwd_call(H_q=0, H_kv=0) == fa.FA_OK
-    assert bwd_call(N_q=0) == fa.FA_OK
     assert fwd_call(N_q=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK
+    # bwd without query rows and without key rows: nothing to write
+    assert bwd_call(N_q=0, N_kv=0) == fa.FA_OK
+    assert bwd_call(B=0) == fa.FA_OK
+    assert bwd_call(H_q=0, H_kv=0) == fa.FA_OK
+
+
+def test_bwd_without_queries_checks_dk_dv():
+    # No query rows but keys present: dk and dv must be zero-filled, so they
+    # are validated (before any HIP call); the other pointers are not used.
+    assert bwd_call(N_q=0, dk=0) == INVALID
+    assert bwd_call(H_q=0, dv=0) == INVALID
+    assert bwd_call(N_q=0, dv=A + 8) == INVALID                # misaligned
+    dk = ptrs(1, A + 64 * STEP)[0]
+    assert bwd_call(N_q=0, dk=dk, dv=dk + 1024) == INVALID     # dk and dv overlap
+    assert bwd_call(N_q=0, N_kv=(1 << 24) + 1) == INVALID
 
 
 def test_output_aliasing_an_input_is_rejected():

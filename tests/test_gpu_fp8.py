@@ -83,11 +83,15 @@ def test_quantizer_two_calls_and_extremes():
 # forward
 # ---------------------------------------------------------------------------
 
-def make_fp8_case(B, H_q, H_kv, N_q, N_kv, d, seed, spread=(-4, 4), zero_v_block=False):
+def make_fp8_case(B, H_q, H_kv, N_q, N_kv, d, seed, spread=(-4, 4), zero_v_block=False, spread_v=None):
+    """Seeded bf16 draws with each 128-row block of Q, K (spread) and V
+    (spread_v, default the same) multiplied by 2^k, k uniform in the range,
+    then quantized by the oracle's block quantizer."""
     inp = make_inputs_shape(DTYPE_BF16, B, H_q, H_kv, N_q, N_kv, d, seed)
     src = {}
     for i, n in enumerate(("q", "k", "v")):
-        bits = block_spread_bits(inp.raw(n), seed + 100 + i, *spread)
+        lo, hi = spread_v if (n == "v" and spread_v is not None) else spread
+        bits = block_spread_bits(inp.raw(n), seed + 100 + i, lo, hi)
         src[n] = bf16_bits_to_f32(bits)
     if zero_v_block and N_kv > 128:
         src["v"][:, :, 128:256] = 0
@@ -111,16 +115,24 @@ def run_fp8(c, causal, scale):
 GAMMA = 2.0 ** -9
 
 
+def _logsumexp_rows(a):
+    m = np.max(a, axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    return (m + np.log(np.sum(np.exp(a - m), axis=1, keepdims=True)))[:, 0]
+
+
 def fp8_bound(c, b, h, G, causal, scale, rows):
     """Bounds for head (b, h), given rows: returns the oracle O and LSE, the
     per-element O bound and the per-row LSE bound.
 
-    Scores: |ds_ij| <= GAMMA * scale * sum_k |q_ik k_jk| (+ float32), at most
-    D_i over the row; the LSE moves by at most D_i and the probabilities by a
-    factor within exp(+-2 D_i). Probability rounding (see fa_fwd_fp8):
-    2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |v_j|. The PV sums: GAMMA of
-    the same sum (the rounded probabilities are at most 1 + 2^-4 of the
-    exact ones, hence the factor 1.07)."""
+    Scores: key j of row i is off by at most delta_ij = GAMMA * scale *
+    sum_k |q_ik k_jk| (the FP8 instruction's summation) plus float32
+    rounding. With w the exact probabilities, the LSE then moves by at most
+    E_i = ln sum_j w_ij exp(delta_ij) (Jensen on both sides), and each
+    probability by a factor within exp(+-(delta_ij + E_i)). Probability
+    rounding (see fa_fwd_fp8): 2^-4 * sum_j max(w_j, 2^-6 wmax / cv_j) |v_j|.
+    The PV sums: GAMMA of the same sum. Everything is formed in the log
+    domain, so the bound is finite whenever the deltas are."""
     hk = h // G
     q = of8.dequantize(c["q8"][b:b + 1, h:h + 1], c["qd"][b:b + 1, h:h + 1])[0, 0]
     k = of8.dequantize(c["k8"][b:b + 1, hk:hk + 1], c["kd"][b:b + 1, hk:hk + 1])[0, 0]
@@ -129,20 +141,29 @@ def fp8_bound(c, b, h, G, causal, scale, rows):
     O, L = oatt.head_forward(q, k, v, causal, scale, rows)
     W = oatt.head_probabilities(q, k, causal, scale, rows)         # exact probabilities
     sig = scale * (np.abs(q[rows]) @ np.abs(k).T)
+    allowed = np.ones_like(sig, dtype=bool)
     if causal:
-        sig = np.where(np.arange(k.shape[0])[None, :] <= rows[:, None], sig, 0.0)
-    D = GAMMA * sig.max(axis=1, keepdims=True) + 1e-6 * (1.0 + np.abs(L)[:, None])
+        allowed = np.arange(k.shape[0])[None, :] <= rows[:, None]
+    delta = np.where(allowed, GAMMA * sig + 1e-6 * (1.0 + np.abs(L)[:, None] + sig), 0.0)
+    # a key whose exact probability underflows (w < e^-700) stays negligible
+    # unless its score can move by hundreds
+    assert float(delta.max()) < 30.0, float(delta.max())
+    with np.errstate(divide="ignore"):
+        logw = np.log(W)
+    E = _logsumexp_rows(np.where(allowed, logw + delta, -np.inf))    # >= 0
+    assert np.all(np.isfinite(E))
+    r = np.expm1(delta + E[:, None])                                   # relative change of each w_ij
     vdb = np.repeat(c["vd"][b, hk].astype(np.float64), 128)[:k.shape[0]]
     cv = np.maximum(64.0 * vdb / max(float(c["vd"][b, hk].max()), 1e-38), 2.0 ** -20)
-    wmax = W.max(axis=1, keepdims=True)                            # = 1 / L
-    eff = np.maximum(W, 2.0 ** -6 * wmax / cv[None, :])
-    grow = np.exp(2.0 * D)
-    wv = W @ np.abs(v)
-    # the PV product runs on the same FP8 instruction: GAMMA of the sum of its
-    # |products| (in output units, w_j |v_j| up to the rounding of P)
-    o_bound = (2.0 ** -4 * (eff @ np.abs(v)) * grow + (grow - 1.0) * wv + GAMMA * (eff @ np.abs(v)) * 1.07
-               + 1e-5 * wv + 1e-6 * np.abs(v).max())
-    return O, L, o_bound, D[:, 0] + 1e-5
+    wmax = W.max(axis=1, keepdims=True)                               # = 1 / L
+    rmax = np.expm1(delta.max(axis=1, keepdims=True) + E[:, None])
+    eff = np.maximum(W * (1.0 + r), 2.0 ** -6 * wmax * (1.0 + rmax) / cv[None, :])
+    av = np.abs(v)
+    wv = W @ av
+    o_bound = ((W * r) @ av + 2.0 ** -4 * (eff @ av) + GAMMA * (eff @ av) * 1.07
+               + 1e-5 * wv + 1e-6 * av.max())
+    assert np.all(np.isfinite(o_bound))
+    return O, L, o_bound, E + 1e-5
 
 
 def check_case(c, B, H_q, H_kv, N_q, causal, scale, rows_per_head=None, seed=0):
@@ -178,8 +199,13 @@ def test_fwd_fp8_ragged_shapes(n_q, n_kv, causal):
 
 
 def test_fwd_fp8_zero_v_block_and_wide_spread():
-    c = make_fp8_case(1, 2, 2, 400, 600, 128, seed=61, spread=(-12, 12), zero_v_block=True)
-    check_case(c, 1, 2, 2, 400, True, default_scale(128))
+    """V blocks spread over 2^-12 .. 2^12 with one all-zero block (so the V
+    scales of the P V product span 24 binades and one is 0), Q and K blocks
+    over 2^-1 .. 2^1."""
+    c = make_fp8_case(1, 2, 2, 400, 600, 128, seed=61, spread=(-1, 1), spread_v=(-12, 12), zero_v_block=True)
+    assert float(c["vd"].max()) / float(c["vd"][c["vd"] > 0].min()) > 2.0 ** 12
+    worst = check_case(c, 1, 2, 2, 400, True, default_scale(128))
+    print(f"largest error as a fraction of its bound: {worst:.3f}")
 
 
 def test_fwd_fp8_uniform_attention_is_exact():

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import (TOL, bf16_half_ulp, default_scale, ensure_library, max_abs, o_within, sample_rows,
-                            to_f64, upload)
+from tests.gpu_util import (TOL, default_scale, ensure_library, max_abs, o_extreme_ok, o_plain_ok, o_small_check,
+                            oracle_forward_all, to_f64, upload)
 from workloads import DTYPE_BF16, DTYPE_F32, WORKLOADS, make_inputs, make_inputs_shape
 
 pytestmark = pytest.mark.gpu
@@ -44,6 +44,7 @@ def test_small_shapes_against_oracle(dtype, d, causal):
     tol = TOL[dtype]
     seed = 100
     worst_o = worst_l = 0.0
+    n_allow = 0
     for (nq, nkv) in PAIRS:
         for (B, Hq, Hkv) in HEADS:
             seed += 1
@@ -54,10 +55,11 @@ def test_small_shapes_against_oracle(dtype, d, causal):
             O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), causal, scale)
             eo, el = max_abs(o, O), max_abs(lse, L)
             assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-            assert o_within(o, O, dtype), (nq, nkv, B, Hq, Hkv, eo)
+            n_allow += o_small_check(o, O, dtype)
             assert el <= tol["lse"], (nq, nkv, B, Hq, Hkv, el)
             worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
-    print(f"worst max-abs O {worst_o:.3e} LSE {worst_l:.3e}")
+    print(f"worst max-abs O {worst_o:.3e} LSE {worst_l:.3e}; elements past the plain 1e-2 bound "
+          f"(all with |O| >= 2): {n_allow}")
 
 
 @pytest.mark.parametrize("dtype", [DTYPE_BF16, DTYPE_F32])
@@ -80,7 +82,7 @@ def test_worked_example_through_the_kernel(dtype):
             torch.cuda.synchronize()
             o = to_f64(o)[0, 0, 0]
             y = np.exp([2.0, 1.0, 3.0]) / np.sum(np.exp([2.0, 1.0, 3.0]))
-            assert o_within(o[:3], y, dtype)
+            assert o_plain_ok(o[:3], y, dtype)
             assert np.all(o[3:] == 0)
             assert abs(float(lse.cpu()[0, 0, 0]) - 3.4076059644) <= TOL[dtype]["lse"]
 
@@ -101,71 +103,42 @@ def test_zero_scale_is_uniform(causal):
         assert abs(lse[0, 1, i] - math.log(n)) <= 1e-3
 
 
-def _row_sample_check(w, inp, o, lse, rng, heads, tol_o, tol_l):
-    """Compare sampled rows of the given (b, h) heads with the oracle
-    (bf16 O: 1e-2 beyond half a bf16 ulp of the exact value, per element)."""
-    G = w.H_q // w.H_kv
-    q = inp.f64("q")
-    k = inp.f64("k")
-    v = inp.f64("v")
-    rows = sample_rows(w.N_q, rng)
-    report = []
-    for (b, h) in heads:
-        hk = h // G
-        O, L = oracle.head_forward(q[b, h], k[b, hk], v[b, hk], w.causal, w.scale, rows)
-        got_o, got_l = o[b, h, rows], lse[b, h, rows]
-        err = np.abs(got_o - O)
-        bound = tol_o + bf16_half_ulp(O)
-        assert np.all(err <= bound), (b, h, float(err.max()), float(np.max(err - bound)))
-        el = max_abs(got_l, L)
-        assert el <= tol_l, (b, h, el)
-        report.append((b, h, float(err.max()), el))
-    return report
-
-
-def _full_output_properties(w, inp, o, lse):
-    """Checks over every output element, at any size: finite; each output row
-    is a convex combination of value rows (within bf16 rounding); for causal
-    rows, LSE_i >= the score with key 0 and with key i."""
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    G = w.H_q // w.H_kv
-    v = inp.f64("v")
-    q = inp.f64("q")
-    k = inp.f64("k")
-    s = oracle.fp32_scale(w.scale)
-    for b in range(w.B):
-        for h in range(w.H_q):
-            hk = h // G
-            # P is rounded to bf16 before the P V product and O is stored in
-            # bf16: allow 2^-7 relative slack on top of the absolute tolerance.
-            slack = 1e-2 + 2.0 ** -7 * np.abs(v[b, hk]).max()
-            vmin = v[b, hk].min(axis=0) - slack
-            vmax = v[b, hk].max(axis=0) + slack
-            assert np.all(o[b, h] >= vmin) and np.all(o[b, h] <= vmax)
-            s0 = s * (q[b, h] @ k[b, hk, 0])
-            assert np.all(lse[b, h] >= s0 - 1e-3)
-            if w.causal and w.N_kv >= w.N_q:
-                sii = s * np.einsum("nd,nd->n", q[b, h], k[b, hk, :w.N_q])
-                assert np.all(lse[b, h] >= sii - 1e-3)
+def _bf16_floor(ref):
+    """max |bf16(ref) - ref|: what rounding the exact output to bf16 costs."""
+    from workloads import f32_to_bf16_bits, bf16_bits_to_f64
+    return float(np.max(np.abs(bf16_bits_to_f64(f32_to_bf16_bits(ref.astype(np.float32))) - ref)))
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4x"])
 def test_config_parity(name):
+    """Every element of O and LSE of the configuration against the oracle,
+    and a second launch on the same device inputs bitwise equal to the first."""
+    import torch
+    import exact_attention_109_amd as fa
     w = WORKLOADS[name]
     print(f"config {name}: {w}", flush=True)
     inp = make_inputs(w)
-    o, lse = run_fwd(inp, w.causal, w.scale)
-    rng = np.random.default_rng(w.seed)
+    q, k, v = upload(inp)
+    o1, l1 = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    o2, l2 = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "two launches differ"
+    o, lse = to_f64(o1), to_f64(l1)
+    del o1, o2, l1, l2, q, k, v
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    O, L = oracle_forward_all(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.causal, w.scale, w.H_q // w.H_kv)
+    eo, el = max_abs(o, O), max_abs(lse, L)
     tol = TOL[w.dtype]
-    if name == "c1":
-        O, L = oracle.attention_forward(inp.f64("q"), inp.f64("k"), inp.f64("v"), w.causal, w.scale)
-        assert max_abs(o, O) <= tol["o"] and max_abs(lse, L) <= tol["lse"]
-        print(f"c1 max-abs O {max_abs(o, O):.3e} LSE {max_abs(lse, L):.3e}")
-        return
-    heads = sorted({(0, 0), (w.B - 1, w.H_q - 1), (0, w.H_q // 2), (w.B - 1, 1 % w.H_q)})
-    rep = _row_sample_check(w, inp, o, lse, rng, heads, tol["o"], tol["lse"])
-    print(f"{name} sampled rows: {rep}")
-    _full_output_properties(w, inp, o, lse)
+    if name == "c4x":
+        floor = _bf16_floor(O)
+        over = int(np.count_nonzero(np.abs(o - O) > tol["o"]))
+        print(f"{name}: max-abs O {eo:.3e} (bf16 floor of the exact O {floor:.3e}, {over} elements past 1e-2, "
+              f"max|O| {np.abs(O).max():.2f}), LSE {el:.3e}")
+        assert o_extreme_ok(o, O), eo
+    else:
+        print(f"{name}: max-abs O {eo:.3e}, LSE {el:.3e}")
+        assert o_plain_ok(o, O, w.dtype), eo
+    assert el <= tol["lse"], el
 
 
 def test_q_zero_closed_form_full_size():

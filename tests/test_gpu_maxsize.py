@@ -10,7 +10,7 @@ import math
 import numpy as np
 import pytest
 
-from tests.gpu_util import ensure_library, o_within, to_f64
+from tests.gpu_util import ensure_library, o_plain_ok, to_f64
 from workloads import DTYPE_BF16
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def test_noncausal_forward_2p24_keys():
     torch.cuda.synchronize()
     rows = [0, 1, 127, 255]
     ref = expected(rows, lambda i: n_kv, d)
-    assert o_within(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
+    assert o_plain_ok(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
     assert np.all(np.abs(to_f64(lse)[0, 0] - math.log(n_kv)) <= 1e-3)
     del k, v
 
@@ -69,7 +69,7 @@ def test_splitkv_decode_2p24_keys():
     torch.cuda.synchronize()
     ref = expected([0], lambda i: n_kv, d)
     for h in range(4):
-        assert o_within(to_f64(o)[0, h, [0]], ref, DTYPE_BF16)
+        assert o_plain_ok(to_f64(o)[0, h, [0]], ref, DTYPE_BF16)
     assert np.all(np.abs(to_f64(lse) - math.log(n_kv)) <= 1e-3)
     del k, v
 
@@ -85,6 +85,6 @@ def test_causal_forward_2p20():
     torch.cuda.synchronize()
     rows = [0, 1, 2, 127, 128, 65535, 65536, n - 257, n - 1]
     ref = expected(rows, lambda i: i + 1, d)
-    assert o_within(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
+    assert o_plain_ok(to_f64(o)[0, 0, rows], ref, DTYPE_BF16)
     got = to_f64(lse)[0, 0, rows]
     assert np.all(np.abs(got - np.log(np.array(rows) + 1.0)) <= 1e-3)

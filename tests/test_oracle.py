@@ -157,6 +157,31 @@ TINY = [(B, Hq, Hkv, nq, nkv, d)
         for d in [1, 4, 8]]
 
 
+def _f32_via_struct(x: float) -> float:
+    """float32 rounding through the C library's double -> float conversion
+    (round to nearest even), independent of numpy."""
+    import struct
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def test_fp32_scale_is_the_float32_value():
+    """The library takes the scale as a C float; the oracle must use exactly
+    that value, not the float64 one (the default 1/sqrt(d) is not a float32
+    number for d = 128)."""
+    x = 1.0 / math.sqrt(128.0)
+    got = oracle.fp32_scale(x)
+    assert got != x                                         # the float64 value is not kept
+    assert got == _f32_via_struct(x)
+    import struct
+    assert struct.pack("<f", got) == bytes.fromhex("f304b53d")  # 0x3DB504F3
+    assert abs(got - x) <= 2.0 ** -28                       # half a float32 ulp in [2^-4, 2^-3)
+    for exact in (0.125, 0.5, 1.0, 0.0, 3.0):               # float32 numbers pass unchanged
+        assert oracle.fp32_scale(exact) == exact
+    # ties round to even: 1 + 2^-24 lies halfway between 1 and 1 + 2^-23
+    assert oracle.fp32_scale(1.0 + 2.0 ** -24) == 1.0
+    assert oracle.fp32_scale(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22
+
+
 @pytest.mark.parametrize("shape", TINY[::3] + TINY[1::7])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bruteforce_matches(shape, causal):
@@ -165,7 +190,7 @@ def test_bruteforce_matches(shape, causal):
     q, k, v = rand_qkv(rng, B, Hq, Hkv, nq, nkv, d)
     scale = 1 / math.sqrt(d)
     O, L = oracle.attention_forward(q, k, v, causal, scale)
-    Ob, Lb = oracle.bruteforce_attention(q.tolist(), k.tolist(), v.tolist(), causal, oracle.fp32_scale(scale))
+    Ob, Lb = oracle.bruteforce_attention(q.tolist(), k.tolist(), v.tolist(), causal, _f32_via_struct(scale))
     assert np.max(np.abs(O - np.array(Ob))) <= 1e-12
     assert np.max(np.abs(L - np.array(Lb))) <= 1e-12
 
