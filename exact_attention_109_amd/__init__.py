@@ -2,7 +2,7 @@
 
 The library's C ABI (include/fa.h) exports fa_fwd, fa_bwd,
 fa_bwd_workspace_size, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
-fa_fwd_varlen, fa_fwd_check, fa_quantize_fp8, fa_fwd_fp8, fa_fwd_splitkv_fp8 and fa_status_string. This module exposes the same names with the same
+fa_fwd_splitkv_noalloc, fa_fwd_varlen, fa_fwd_check, fa_quantize_fp8, fa_fwd_fp8, fa_fwd_splitkv_fp8 and fa_status_string. This module exposes the same names with the same
 arguments (device pointers as integers, sizes, flags, a stream handle) plus
 convenience wrappers over torch tensors:
 
@@ -36,6 +36,7 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
 
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_size.restype = sz
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
@@ -105,6 +108,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, d
                    workspace_bytes, stream) -> int:
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, int(causal), float(scale),
                                          dtype, num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal, scale, dtype, num_splits,
+                           stream) -> int:
+    return load_library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, int(causal),
+                                                 float(scale), dtype, num_splits, stream)
 
 
 def fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits) -> int:
@@ -320,6 +329,7 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
 
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES",
            "fa_fwd_varlen", "fa_fwd_check", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "fwd_check", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
            "FA_DTYPE_BF16", "LIB_PATH"]

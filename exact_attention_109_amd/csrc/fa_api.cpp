@@ -180,13 +180,15 @@ FA_EXPORT size_t fa_fwd_splitkv_workspace_size(int B, int H_q, int N_q, int d, i
   return (bytes + 255) & ~size_t(255);
 }
 
-FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int B, int H_q, int H_kv, int N_q, int N_kv, int d,
-                             int causal, float scale, int dtype, int num_splits,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-  bool empty = false;
-  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, &empty);
-  if (rc != FA_OK || empty) return rc;
+namespace {
+
+// Checks shared by fa_fwd_splitkv and fa_fwd_splitkv_noalloc, up to (not
+// including) the workspace. Sets *empty when there is nothing to do.
+int check_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H_q, int H_kv,
+                  int N_q, int N_kv, int d, float scale, int dtype, int num_splits, bool* empty,
+                  Range in[3], Range out[2]) {
+  int rc = check_shape(B, H_q, H_kv, N_q, N_kv, d, scale, dtype, empty);
+  if (rc != FA_OK || *empty) return rc;
 
   const size_t es = elem_size(dtype);
   const size_t q_bytes = size_t(B) * H_q * N_q * d * es;
@@ -195,16 +197,32 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  const Range in[3] = {range_of(q, q_bytes), range_of(k, kv_bytes), range_of(v, kv_bytes)};
-  const Range out[2] = {range_of(o, q_bytes), range_of(lse, lse_bytes)};
-  for (const Range& r : out)
-    for (const Range& i : in)
-      if (overlaps(r, i)) return FA_ERR_INVALID_ARG;
+  in[0] = range_of(q, q_bytes);
+  in[1] = range_of(k, kv_bytes);
+  in[2] = range_of(v, kv_bytes);
+  out[0] = range_of(o, q_bytes);
+  out[1] = range_of(lse, lse_bytes);
+  for (int r = 0; r < 2; ++r)
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(out[r], in[i])) return FA_ERR_INVALID_ARG;
   if (overlaps(out[0], out[1])) return FA_ERR_INVALID_ARG;
 
   if (num_splits < 1 || num_splits > 256) return FA_ERR_INVALID_ARG;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if ((H_q / H_kv) * N_q > 32) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                             int causal, float scale, int dtype, int num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  Range in[3], out[2];
+  int rc = check_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, scale, dtype, num_splits, &empty, in, out);
+  if (rc != FA_OK || empty) return rc;
 
   const size_t ws_need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits);
   if (ws_need > 0) {
@@ -222,6 +240,26 @@ FA_EXPORT int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   fa::FwdParams p{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
   hipError_t err = fa::launch_fwd_split_bf16(p, num_splits, static_cast<float*>(workspace),
                                              reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_EXPORT int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                                     int causal, float scale, int dtype, int num_splits, void* stream) {
+  bool empty = false;
+  Range in[3], out[2];
+  int rc = check_splitkv(q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, scale, dtype, num_splits, &empty, in, out);
+  if (rc != FA_OK || empty) return rc;
+  const size_t ws_need = fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits);
+  if (ws_need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_INVALID_ARG;
+
+  rc = check_device();
+  if (rc != FA_OK) return rc;
+  float* ws = nullptr;
+  if (ws_need > 0 && fa::split_scratch_pointer(&ws) != hipSuccess) return FA_ERR_HIP;
+
+  fa::FwdParams p{q, k, v, o, lse, B, H_q, H_kv, N_q, N_kv, d, causal ? 1 : 0, scale};
+  hipError_t err = fa::launch_fwd_split_bf16(p, num_splits, ws, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -28,6 +28,10 @@
 //  * A second kernel merges the key ranges of every row in a fixed order
 //    (deterministic): LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
 
+#include <atomic>
+#include <mutex>
+
+#include "fa.h"
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -689,6 +693,45 @@ hipError_t launch_fwd_split_fp8kv(const SplitFp8Params& p, int num_splits, float
                     : launch_fp8kv<128, false>(p, num_splits, workspace, stream);
   return p.causal ? launch_fp8kv<64, true>(p, num_splits, workspace, stream)
                   : launch_fp8kv<64, false>(p, num_splits, workspace, stream);
+}
+
+}  // namespace fa
+
+// ---- Statically reserved partials for the entry point that allocates
+// nothing. In host code `scratch` names a host-side stand-in of the array,
+// not its device address, so it is never handed to a kernel or a copy: the
+// address each device holds it at is looked up once per device with
+// hipGetSymbolAddress (with that device current) and cached.
+namespace fa {
+namespace {
+
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+hipError_t split_scratch_pointer(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || addr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -60,6 +60,9 @@ hipError_t launch_check(const FwdParams& p, const int* rows, int n_rows, float* 
 // fwd_split_workspace_floats(...) floats when num_splits > 1.
 hipError_t launch_fwd_split_bf16(const FwdParams& p, int num_splits, float* workspace, hipStream_t stream);
 size_t fwd_split_workspace_floats(int B, int H_q, int N_q, int d, int num_splits);
+// Device address of the statically reserved split-KV partials array
+// (FA_NOALLOC_SCRATCH_BYTES) on the current device, looked up once per device.
+hipError_t split_scratch_pointer(float** out);
 
 // FP8 forward: e4m3 codes with one float32 descale per 128-row block, all
 // row-major; o is bf16, lse float32.

@@ -163,6 +163,33 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int causal, float scale, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the statically reserved device array fa_fwd_splitkv_noalloc uses
+ * in place of a workspace (per device, held until the process ends). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that must not call an allocator, harnesses that forbid it.
+ *
+ * Same arguments (minus workspace and workspace_bytes), checks, kernels and
+ * results as fa_fwd_splitkv. The key-range partials live in a device array
+ * of FA_NOALLOC_SCRATCH_BYTES that the library reserves statically on every
+ * device it runs on (its address is looked up on the first call on a device)
+ * and that stays reserved until the process ends. The call allocates and
+ * frees nothing. Every (row, key range) partial is rewritten by each call, so
+ * the array's content on entry does not matter.
+ * Errors: as fa_fwd_splitkv, plus FA_ERR_INVALID_ARG (before any HIP call)
+ * when fa_fwd_splitkv_workspace_size(B, H_q, N_q, d, num_splits) exceeds
+ * FA_NOALLOC_SCRATCH_BYTES, and FA_ERR_HIP if the array's address cannot be
+ * obtained. All calls on one device share the array: calls that may run at
+ * the same time on one device (different streams, or different host threads
+ * without ordering) race and give wrong results; order them on one stream.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H_q, int H_kv, int N_q, int N_kv, int d,
+                           int causal, float scale, int dtype, int num_splits, void* stream);
+
 /*
  * fa_fwd_varlen -- attention forward over a batch of sequences of different
  * lengths, packed without padding.

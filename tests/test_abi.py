@@ -29,8 +29,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_check", "fa_fwd_fp8",
-                                    "fa_fwd_splitkv", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_workspace_size",
-                                    "fa_fwd_varlen", "fa_quantize_fp8", "fa_status_string"]
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_noalloc",
+                                    "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_quantize_fp8",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -371,3 +372,27 @@ def test_splitkv_fp8_invalid_arguments(kw, expect):
 def test_splitkv_fp8_empty_is_a_noop():
     assert split8_call(N_q=0) == fa.FA_OK
     assert split8_call(B=0) == fa.FA_OK
+
+
+def noalloc_call(**kw):
+    q, k, v, o, lse = ptrs(5)
+    args = dict(q=q, k=k, v=v, o=o, lse=lse, B=2, H_q=8, H_kv=2, N_q=1, N_kv=4096, d=128, causal=0,
+                scale=0.088, dtype=fa.FA_DTYPE_BF16, num_splits=8, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(**args)
+
+
+def test_splitkv_noalloc_checks():
+    # the limit of the static partials array is enforced before any HIP call
+    assert fa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    big = dict(B=64, H_q=32, H_kv=8, N_q=1, N_kv=4096, num_splits=256)
+    assert fa.fa_fwd_splitkv_workspace_size(64, 32, 1, 128, 256) > fa.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(**big) == INVALID
+    # the checks shared with fa_fwd_splitkv
+    assert noalloc_call(num_splits=0) == INVALID
+    assert noalloc_call(num_splits=257) == INVALID
+    assert noalloc_call(dtype=fa.FA_DTYPE_F32) == UNSUP
+    assert noalloc_call(N_q=5, H_q=8, H_kv=1) == UNSUP          # 40 rows per key/value head
+    assert noalloc_call(q=0) == INVALID
+    assert noalloc_call(o=ptrs(1)[0]) == INVALID               # o aliases q
+    assert noalloc_call(N_q=0) == fa.FA_OK                     # empty: nothing launched
