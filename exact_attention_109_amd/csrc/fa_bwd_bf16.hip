@@ -11,14 +11,14 @@
 //
 // Three kernels on one stream, no atomics (deterministic):
 //  * pre:  D_i and lse_i*log2(e) for every query row (HBM-bound pass over O, dO).
-//  * dkdv: one workgroup per (batch, key/value head, 128-key tile); each wave
-//          owns 32 keys and keeps their K and V as MFMA operands in
-//          registers, while the query blocks of every query head of the
-//          group stream past through LDS. Per 64-query block and wave:
-//          S = Q K^T and dP = dO V^T (queries x keys, Q/dO rows read from LDS),
-//          P and dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS with the
-//          dO/Q operands read transposed (ds_read_b64_tr_b16). Software-
-//          pipelined like dq below.
+//  * dkdv: one workgroup of 8 waves per (batch, key/value head, 128-key
+//          tile); the two waves of each SIMD share 32 keys: one keeps K as
+//          its MFMA operand and forms S = Q K^T, P and dV^T += dO^T P, the
+//          other keeps V and forms dP = dO V^T, dS = P (dP - D) and
+//          dK^T += Q^T dS, with P handed over through LDS, so that one's
+//          exponentials run beside the other's MFMAs. The query blocks of
+//          every query head of the group stream past through LDS (dO and Q
+//          read transposed with ds_read_b64_tr_b16 for dV and dK).
 //  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
 //          owns 32 queries (Q and dO as register operands) while the K/V
 //          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
@@ -124,8 +124,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // Shared pieces of the two main kernels
 // ---------------------------------------------------------------------------
-constexpr int kNBuf = 4;  // LDS buffers of the dK/dV kernel's streamed blocks: two in use, two loading
-
 // sched_group_barrier instruction classes
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
@@ -141,92 +139,106 @@ __device__ __forceinline__ void schedule_mfma_reads() {
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, READS_PER_MFMA, 0);
   }
 }
-// ---------------------------------------------------------------------------
-// dK, dV
-// ---------------------------------------------------------------------------
-constexpr int kKeysPerWg = 128;  // 4 waves x 32 keys
+constexpr int kKeysPerWg = 128;  // keys per dK/dV workgroup: 4 wave pairs x 32 keys
 
-// Per wave (32 keys, K and V as register operands) and streamed query block
-// jb (64 queries of one query head):
-//   X(jb): S = Q K^T, dP = dO V^T                      (MFMA, Q/dO rows from LDS)
-//   Y(jb): P = exp2(S c - L2), dS = P (dP - D), packed  (VALU)
-//   Z(jb): dV^T += dO^T P, dK^T += Q^T dS               (MFMA, Q/dO read transposed)
-// Iteration jb runs Y(jb) interleaved with X(jb+1) (S/dP double-buffered),
-// then Z(jb); the LDS-DMA of block jb+3 is issued between the vector work.
+// ---------------------------------------------------------------------------
+// dK, dV with wave pairs (two waves per SIMD)
+// ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (batch, key/value head, 128-key tile). Waves w
+// and w + 4 (w = 0..3) run on the same SIMD and own the same 32 keys:
+//   P wave  (w):     S = Q K^T, P = exp2(S c - L2) (masked), dV^T += dO^T P
+//   dS wave (w + 4): dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+// P goes from the P wave to its dS wave through LDS in float32, lane for lane
+// (both waves compute their scores in the same accumulator layout, so lane l
+// register i of one is lane l register i of the other). Two ticks per query
+// block j, each ended by a workgroup barrier:
+//   tick 1: P wave:  S(j), then P(j) and its hand-over (vector work);
+//           dS wave: dK += Q(j-1)^T dS(j-1), then dP(j)          (MFMA)
+//   tick 2: P wave:  dV += dO(j)^T P(j)                            (MFMA);
+//           dS wave: dS(j) (vector work), LDS-DMA of block j+2, wait for j+1
+// so on each SIMD one wave's contractions run while the other does its
+// vector work, with the four contractions per block of the textbook
+// backward. Each wave keeps one 32-key operand and one accumulator set, about
+// half the registers of a wave that owns both, which is what lets two waves
+// share a SIMD. Query blocks are streamed from the last one down, so the
+// workgroups of all key tiles of a head start on the same block (shared
+// through L2) instead of each at its own diagonal.
+constexpr int kPairThreads = 512;
+constexpr int kPairRing = 3;  // Q / dO / vector buffers: blocks j-1 (dK of the dS wave), j, j+1; j+2 loads into j-1's
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): this wave's
+// LDS writes are complete.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     float* __restrict__ dK, float* __restrict__ dV, int H_q, int H_kv, int N_q, int N_kv, int n_ktiles,
     int xcd_remap, float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int BQ = C::BLK;
-  constexpr int DPW = C::DMA_PER_WAVE;
-  __shared__ __attribute__((aligned(1024))) uint8_t qs[kNBuf][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t os[kNBuf][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) float vecs[kNBuf][2][BQ];  // [buffer][L2, D][query]
+  constexpr int DPW = C::DMA_PER_WAVE;   // 1 KiB pieces of a tile per loading (dS) wave
+  constexpr int NG = C::NSUB * 4;        // groups of 4 score registers per lane
+  __shared__ __attribute__((aligned(1024))) uint8_t qs[kPairRing][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t os[kPairRing][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float vecs[kPairRing][2][BQ];  // [buffer][L2, D][query]
+  __shared__ __attribute__((aligned(1024))) f32x4 pex[4][NG][64];         // [pair][register group][lane]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = wave & 3;         // pair index = 32-key sub-tile = SIMD
+  const bool is_ds = wave >= 4;    // wave-uniform role
   const int col = lane & 31;
   const int half = lane >> 5;
   const int G = H_q / H_kv;
 
-  // key tiles: the first ones see the most queries when causal, so they go first
   const TileAssign ta = assign_tile(blockIdx.x, n_ktiles, 1, xcd_remap);
   const int b = ta.kvidx / H_kv;
   const int hk = ta.kvidx % H_kv;
   const int k0 = ta.tile_rank * kKeysPerWg;
-  const int kw = k0 + 32 * wave;   // first key of this wave
+  const int kw = k0 + 32 * pw;     // first key of this pair
   const int key = kw + col;        // this lane's key (MFMA column)
-
   const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
-  // K and V of this wave's 32 keys as B operands (k = head dimension)
-  bf16x8 kreg[C::KST], vreg[C::KST];
+
+  // This wave's B operand over the head dimension: K (P wave) or V (dS
+  // wave) of its 32 keys.
+  bf16x8 kv[C::KST];
   {
+    const uint16_t* src = is_ds ? V : K;
     const size_t off = kvbase + size_t(min(key, N_kv - 1)) * D + half * (D / 2);
 #pragma unroll
-    for (int t = 0; t < C::KST; ++t) {
-      kreg[t] = as_bf16x8(ld_global16(K + off + 8 * t));
-      vreg[t] = as_bf16x8(ld_global16(V + off + 8 * t));
-    }
-    // only MFMAs read these: keep them in AGPRs, out of the vector work's way
-#pragma unroll
-    for (int t = 0; t < C::KST; ++t) asm volatile("" : "+a"(kreg[t]), "+a"(vreg[t]));
+    for (int t = 0; t < C::KST; ++t) kv[t] = as_bf16x8(ld_global16(src + off + 8 * t));
   }
   wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
 
-  // query blocks: for each of the G query heads, blocks from qstart to N_q.
-  // Every wave runs every block of the workgroup (blocks before a wave's keys
-  // are masked to zero).
   const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
   const int nqb = qstart < N_q ? (N_q - qstart + BQ - 1) / BQ : 0;
   const int nblk = G * nqb;
 
-  // LDS-DMA of a block: per-lane offsets within a tile, and clamped ones for
-  // the partial last block of a head (rows past N_q repeat row N_q - 1).
+  auto block_head = [&](int jb, int& h, int& qb0) __attribute__((always_inline)) {
+    const int g = jb / nqb;
+    h = hk * G + g;
+    qb0 = qstart + (nqb - 1 - jb % nqb) * BQ;  // the head's blocks from the last one down
+  };
+
+  // LDS-DMA of a block by the 4 dS waves: each loads DPW 1 KiB pieces of the
+  // Q and of the dO tile; dS waves 0 and 1 also load the 64 L2 and D values.
+  // The partial last block of a head reads row N_q - 1 for the rows past it.
   const int tail_q0 = (N_q % BQ) ? N_q - N_q % BQ : -1;
   const int tail_lim = (N_q - 1) % BQ;
   uint32_t doff[DPW], doff_t[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
-    const int ig = wave * DPW + i;
+    const int ig = pw * DPW + i;
     const int row = C::RPI * ig + lane / C::CPR;
     const int pch = lane % C::CPR;
     doff[i] = row * C::ROW_BYTES + (pch ^ swz<D>(row)) * 16;
     doff_t[i] = doff[i] - (row - min(row, tail_lim)) * C::ROW_BYTES;
   }
   const uint32_t voff = lane * 4, voff_t = min(lane, tail_lim) * 4;
-  const float* vsrc = (wave & 1) ? Dl : L2;  // waves 0, 2: L2; waves 1, 3: D (same bytes twice)
-
-  auto block_head = [&](int jb, int& h, int& qb0) __attribute__((always_inline)) {
-    const int g = jb / nqb;
-    h = hk * G + g;
-    qb0 = qstart + (jb % nqb) * BQ;
-  };
-  // DMA slot i of block jb into buffer bf: Q pieces, dO pieces, then the vector.
-  constexpr int kSlots = 2 * DPW + 1;
+  const float* vsrc = pw == 0 ? L2 : Dl;
   auto dma_slot = [&](int i, int jb, int bf) __attribute__((always_inline)) {
     int h, qb0;
     block_head(jb, h, qb0);
@@ -237,51 +249,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const int ii = is_q ? i : i - DPW;
       const uint8_t* src = reinterpret_cast<const uint8_t*>((is_q ? Q : dO) + (rbase + qb0) * D);
       lds_dma16_sbase_nc(src, tail ? doff_t[ii] : doff[ii],
-                         lds_address(is_q ? qs[bf] : os[bf]) + 1024 * (wave * DPW + ii));
+                         lds_address(is_q ? qs[bf] : os[bf]) + 1024 * (pw * DPW + ii));
     } else {
-      lds_dma4_sbase_nc(vsrc + rbase + qb0, tail ? voff_t : voff, lds_address(&vecs[bf][wave & 1][0]));
+      lds_dma4_sbase_nc(vsrc + rbase + qb0, tail ? voff_t : voff, lds_address(&vecs[bf][pw][0]));
     }
+  };
+  // DMA instructions per dS wave and block: waves 0 and 1 add a vector load
+  const int n_slots = 2 * DPW + (pw < 2 ? 1 : 0);
+  auto dma_block = [&](int jb, int bf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2 * DPW; ++i) dma_slot(i, jb, bf);
+    if (pw < 2) dma_slot(2 * DPW, jb, bf);
   };
 
   ReadOffsets<D> ro;
   ro.init(lane);
 
-  f32x16 dk[C::DSUB], dv[C::DSUB];
-#pragma unroll
-  for (int s = 0; s < C::DSUB; ++s) {
-    dk[s] = f32x16{};
-    dv[s] = f32x16{};
-  }
-  f32x16 sA[C::NSUB], pA[C::NSUB], sB[C::NSUB], pB[C::NSUB];  // S, dP of two blocks
-  u32x4 pk[C::STEPS], sk[C::STEPS];                            // P, dS (bf16) of the current block
-
-  constexpr int NX = 2 * C::KST * C::NSUB;    // MFMAs of X
-  constexpr int NZ = 2 * C::STEPS * C::DSUB;  // MFMAs of Z
-  auto X = [&](int bf, f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
-    const uint8_t* qt = qs[bf];
-    const uint8_t* ot = os[bf];
-#pragma unroll
-    for (int n = 0; n < C::NSUB; ++n) {
-      sx[n] = f32x16{};
-      px[n] = f32x16{};
-    }
-#pragma unroll
-    for (int t = 0; t < C::KST; ++t) {
-#pragma unroll
-      for (int n = 0; n < C::NSUB; ++n) {
-        const int o = ro.row[t] + n * 32 * C::ROW_BYTES;
-        sx[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o)), kreg[t], sx[n]);
-        px[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o)), vreg[t], px[n]);
-      }
-    }
+  auto need_mask = [&](int jb) __attribute__((always_inline)) {
+    int h, qb0;
+    block_head(jb, h, qb0);
+    (void)h;
+    return (CAUSAL && qb0 < kw + 31) || (qb0 + BQ > N_q);
   };
   // Scores of block jb that no query may attend (query before this lane's
-  // key, or past N_q) become -inf, so that P and dS are exactly 0 there.
+  // key, or past N_q) become -inf, so that P, and with it dS, are exactly 0.
   auto mask_scores = [&](int jb, f32x16 (&sx)[C::NSUB]) __attribute__((always_inline)) {
     int h, qb0;
     block_head(jb, h, qb0);
     (void)h;
-    // query 32n + 16*half + i of the block is visible iff lo <= 32n + i <= hi
     const int lo = CAUSAL ? key - qb0 - 16 * half : INT_MIN;
     const int hi = N_q - 1 - qb0 - 16 * half;
 #pragma unroll
@@ -290,131 +285,177 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int i = 0; i < 16; ++i)
         if (32 * n + i < lo || 32 * n + i > hi) sx[n][i] = -INFINITY;
   };
-  // Y(jb) on (s, p) from buffer bfy -> (pk, sk); with WITH_X also X(jb+1)
-  // from buffer bfx into (sx, px) and the DMA of block jd into buffer bfd.
-  auto YX = [&](auto with_x, int bfy, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], int bfx,
-                f32x16 (&sx)[C::NSUB], f32x16 (&px)[C::NSUB], int jd, int bfd) __attribute__((always_inline)) {
-    constexpr bool WITH_X = decltype(with_x)::value;
-    if constexpr (WITH_X) X(bfx, sx, px);
-    const float* lt = vecs[bfy][0];
-    const float* dt = vecs[bfy][1];
+  // 16 MFMAs: acc[n] = rows of tile t_rows (Q or dO, rows from LDS) times kv
+  auto rows_times_kv = [&](const uint8_t* tile, f32x16 (&acc)[C::NSUB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int n = 0; n < C::NSUB; ++n) {
+    for (int n = 0; n < C::NSUB; ++n) acc[n] = f32x16{};
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 32 * n + 16 * half + 4 * v4);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(dt + 32 * n + 16 * half + 4 * v4);
+    for (int t = 0; t < C::KST; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * v4 + e;
-          const float pv = fast_exp2(fmaf(s[n][i], c, -a[e]));
-          s[n][i] = pv;
-          p[n][i] = pv * (p[n][i] - d[e]);
-          if constexpr (WITH_X) {
-            const int el = 16 * n + i;
-            if (el % 3 == 1 && el / 3 < kSlots) dma_slot(el / 3, jd, bfd);
-          }
-        }
-      }
-#pragma unroll
-      for (int w = 0; w < 2; ++w)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pk[2 * n + w][e] = cvt_pk_bf16(s[n][8 * w + 2 * e], s[n][8 * w + 2 * e + 1]);
-          sk[2 * n + w][e] = cvt_pk_bf16(p[n][8 * w + 2 * e], p[n][8 * w + 2 * e + 1]);
-        }
-    }
-    if constexpr (WITH_X) {
-#pragma unroll
-      for (int e = 16 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
-    }
+      for (int n = 0; n < C::NSUB; ++n)
+        acc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(tile + ro.row[t] + n * 32 * C::ROW_BYTES)),
+                              kv[t], acc[n]);
   };
-  auto Z = [&](int bf) __attribute__((always_inline)) {
-    const uint8_t* qt = qs[bf];
-    const uint8_t* ot = os[bf];
+  // 16 MFMAs: out[s] += tile^T (transposed reads) times the packed block operand
+  auto tileT_times = [&](const uint8_t* tile, const u32x4 (&pk)[C::STEPS], f32x16 (&out)[C::DSUB])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < C::STEPS; ++u) {
       const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
 #pragma unroll
-      for (int s = 0; s < C::DSUB; ++s) {
-        const bf16x8 ao = lds_read_tr8(ot + ro.tr[s][0] + rb, ot + ro.tr[s][1] + rb);
-        dv[s] = mfma32x32x16(ao, as_bf16x8(pk[u]), dv[s]);
-        const bf16x8 aq = lds_read_tr8(qt + ro.tr[s][0] + rb, qt + ro.tr[s][1] + rb);
-        dk[s] = mfma32x32x16(aq, as_bf16x8(sk[u]), dk[s]);
-      }
+      for (int s = 0; s < C::DSUB; ++s)
+        out[s] = mfma32x32x16(lds_read_tr8(tile + ro.tr[s][0] + rb, tile + ro.tr[s][1] + rb), as_bf16x8(pk[u]), out[s]);
     }
-    schedule_mfma_reads<NZ - 4, 2, 8>();
   };
-  auto need_mask = [&](int jb) __attribute__((always_inline)) {
-    int h, qb0;
-    block_head(jb, h, qb0);
-    (void)h;
-    return (CAUSAL && qb0 < kw + 31) || (qb0 + BQ > N_q);
-  };
-  // iteration jb (< nblk - 1): Y(jb) on (s, p) with X(jb+1) into (sx, px), then Z(jb)
-  auto iteration = [&](int jb, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB], f32x16 (&sx)[C::NSUB],
-                       f32x16 (&px)[C::NSUB]) __attribute__((always_inline)) {
-    const int jd = min(jb + 3, nblk - 1);  // past the end: a harmless reload into a free buffer
-    if (need_mask(jb)) mask_scores(jb, s);
-    __builtin_amdgcn_sched_barrier(0);
-    YX(std::true_type{}, jb % kNBuf, s, p, (jb + 1) % kNBuf, sx, px, jd, (jb + 3) % kNBuf);
-    __builtin_amdgcn_sched_barrier(0);
-    Z(jb % kNBuf);
-    wait_vmem_keep<kSlots>();  // block jb+2 (loaded since the last iteration) is in LDS
-    barrier_nofence();
-  };
-  auto last = [&](int jb, f32x16 (&s)[C::NSUB], f32x16 (&p)[C::NSUB]) __attribute__((always_inline)) {
-    if (need_mask(jb)) mask_scores(jb, s);
-    __builtin_amdgcn_sched_barrier(0);
-    YX(std::false_type{}, jb % kNBuf, s, p, 0, sB, pB, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    Z(jb % kNBuf);
-  };
+  constexpr int NX = C::KST * C::NSUB;   // MFMAs of one rows_times_kv
+  constexpr int NZ = C::STEPS * C::DSUB; // MFMAs of one tileT_times
 
-  if (nblk > 0) {
-    // blocks 0, 1, 2 into buffers 0, 1, 2, X(0), then the pipeline
+  f32x16 acc[C::DSUB];  // dV^T (P wave) or dK^T (dS wave): lane = key, registers = head-dimension columns
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) dma_slot(i, min(1, nblk - 1), 1);
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) dma_slot(i, min(2, nblk - 1), 2);
+  for (int s = 0; s < C::DSUB; ++s) acc[s] = f32x16{};
+
+  // ---- prologue: blocks 0 and 1 into buffers 0 and 1
+  if (is_ds && nblk > 0) {
+    dma_block(0, 0);
+    dma_block(min(1, nblk - 1), 1);
     wait_vmem();
-    __syncthreads();
-    X(0, sA, pA);
-    schedule_mfma_reads<NX - 4, 1, 4>();
-    __builtin_amdgcn_sched_barrier(0);
-    int jb = 0;
-    for (; jb + 2 < nblk; jb += 2) {
-      iteration(jb, sA, pA, sB, pB);
-      iteration(jb + 1, sB, pB, sA, pA);
-    }
-    if (jb + 1 < nblk) {
-      iteration(jb, sA, pA, sB, pB);
-      last(jb + 1, sB, pB);
-    } else {
-      last(jb, sA, pA);
-    }
   }
+  __syncthreads();
 
-  // dK^T / dV^T accumulators: lane = key, register 4a+b of subtile s = column 32s + 8a + 4*half + b
-  if (key < N_kv) {
-    float* dkp = dK + kvbase + size_t(key) * D;
-    float* dvp = dV + kvbase + size_t(key) * D;
+  if (!is_ds) {
+    // ------------------------------------------------------------ P wave
+    f32x16 sx[C::NSUB];
+    u32x4 pk[C::STEPS];
+    // block j in ring buffer BF (a compile-time constant, so that every LDS
+    // address is a per-lane offset plus an immediate)
+    auto p_block = [&](int j, auto bfc) __attribute__((always_inline)) {
+      constexpr int BF = decltype(bfc)::value;
+      // tick 1: S(j), P(j), hand-over
+      __builtin_amdgcn_s_setprio(1);  // S(j) first: the vector work after it is this tick's longer side
+      __builtin_amdgcn_sched_barrier(0);
+      rows_times_kv(qs[BF], sx);
+      schedule_mfma_reads<NX - 4, 1, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      if (need_mask(j)) mask_scores(j, sx);
+      const float* lt = vecs[BF][0];
 #pragma unroll
-    for (int s = 0; s < C::DSUB; ++s)
+      for (int n = 0; n < C::NSUB; ++n) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        f32x4 vk, vv;
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 32 * n + 16 * half + 4 * v4);
+          f32x4 pv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vk[e] = dk[s][4 * a + e] * scale;
-          vv[e] = dv[s][4 * a + e];
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = fast_exp2(fmaf(sx[n][4 * v4 + e], c, -a[e]));
+            sx[n][4 * v4 + e] = pv[e];
+          }
+          pex[pw][4 * n + v4][lane] = pv;
         }
-        *reinterpret_cast<f32x4*>(dkp + 32 * s + 8 * a + 4 * half) = vk;
-        *reinterpret_cast<f32x4*>(dvp + 32 * s + 8 * a + 4 * half) = vv;
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[2 * n + w][e] = cvt_pk_bf16(sx[n][8 * w + 2 * e], sx[n][8 * w + 2 * e + 1]);
       }
+      wait_lds();          // P(j) is in LDS before the barrier hands it over
+      barrier_nofence();
+      // tick 2: dV += dO(j)^T P(j)
+      tileT_times(os[BF], pk, acc);
+      schedule_mfma_reads<NZ - 4, 2, 8>();
+      barrier_nofence();
+    };
+    for (int j = 0; j < nblk; j += kPairRing) {
+      p_block(j, std::integral_constant<int, 0>{});
+      if (j + 1 < nblk) p_block(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 < nblk) p_block(j + 2, std::integral_constant<int, 2>{});
+    }
+    if (key < N_kv) {
+      float* dvp = dV + kvbase + size_t(key) * D;
+#pragma unroll
+      for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = acc[s][4 * a + e];
+          *reinterpret_cast<f32x4*>(dvp + 32 * s + 8 * a + 4 * half) = vv;
+        }
+    }
+  } else {
+    // ----------------------------------------------------------- dS wave
+    f32x16 px[C::NSUB];
+    u32x4 sk[C::STEPS];
+    auto ds_block = [&](int j, auto bfc) __attribute__((always_inline)) {
+      constexpr int BF = decltype(bfc)::value;
+      constexpr int BFP = (BF + kPairRing - 1) % kPairRing;  // block j-1, and j+2's DMA target
+      // tick 1: dK += Q(j-1)^T dS(j-1), dP(j)
+      if (j >= 1) {
+        tileT_times(qs[BFP], sk, acc);
+        schedule_mfma_reads<NZ - 4, 2, 8>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rows_times_kv(os[BF], px);
+      schedule_mfma_reads<NX - 4, 1, 4>();
+      barrier_nofence();
+      // tick 2: dS(j) = P(j) (dP(j) - D), DMA of block j+2, wait for block j+1
+      const int jd = min(j + 2, nblk - 1);  // past the end: a harmless reload into a free buffer
+      const float* dt = vecs[BF][1];
+#pragma unroll
+      for (int n = 0; n < C::NSUB; ++n) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 32 * n + 16 * half + 4 * v4);
+          const f32x4 pv = pex[pw][4 * n + v4][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) px[n][4 * v4 + e] = pv[e] * (px[n][4 * v4 + e] - d4[e]);
+          const int slot = 4 * n + v4;
+          if (slot < 2 * DPW) dma_slot(slot, jd, BFP);
+        }
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(px[n][8 * w + 2 * e], px[n][8 * w + 2 * e + 1]);
+      }
+#pragma unroll
+      for (int slot = 4 * C::NSUB; slot < 2 * DPW; ++slot) dma_slot(slot, jd, BFP);
+      if (pw < 2) {
+        dma_slot(2 * DPW, jd, BFP);
+        wait_vmem_keep<2 * DPW + 1>();   // block j+1 (loaded during block j-1) is in LDS
+      } else {
+        wait_vmem_keep<2 * DPW>();
+      }
+      barrier_nofence();
+    };
+    int j = 0;
+    for (; j + kPairRing <= nblk; j += kPairRing) {
+      ds_block(j, std::integral_constant<int, 0>{});
+      ds_block(j + 1, std::integral_constant<int, 1>{});
+      ds_block(j + 2, std::integral_constant<int, 2>{});
+    }
+    // the remaining 0-2 blocks, then dK of the last block
+    if (j < nblk) ds_block(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nblk) ds_block(j + 1, std::integral_constant<int, 1>{});
+    if (nblk > 0) {
+      const int bl = (nblk - 1) % kPairRing;
+      if (bl == 0) tileT_times(qs[0], sk, acc);
+      else if (bl == 1) tileT_times(qs[1], sk, acc);
+      else tileT_times(qs[2], sk, acc);
+    }
+    wait_vmem();  // the reloads past the end land before the workgroup's LDS is released
+    if (key < N_kv) {
+      float* dkp = dK + kvbase + size_t(key) * D;
+#pragma unroll
+      for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 vk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vk[e] = acc[s][4 * a + e] * scale;
+          *reinterpret_cast<f32x4*>(dkp + 32 * s + 8 * a + 4 * half) = vk;
+        }
+    }
   }
+  (void)n_slots;
 }
 
 // ---------------------------------------------------------------------------
@@ -436,8 +477,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
-    float* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, float c,
-    float scale) {
+    float* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, int B_heads,
+    float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int BK = C::BLK;
   constexpr int DPW = C::DMA_PER_WAVE;
@@ -452,7 +493,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int half = lane >> 5;
   const int G = H_q / H_kv;
 
-  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap);
+  // two workgroups per compute unit and few tiles each: deal them heaviest
+  // first across all heads (rank-major)
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, B_heads, true);
   const int b = ta.kvidx / H_kv;
   const int hk = ta.kvidx % H_kv;
   const int h = hk * G + ta.gq;
@@ -621,15 +664,15 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
   const int n_ktiles = (p.N_kv + kKeysPerWg - 1) / kKeysPerWg;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_ktiles * p.B * p.H_kv)),
-                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_ktiles * p.B * p.H_kv)),
+                     dim3(kPairThreads), 0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dk, p.dv,
                      p.H_q, p.H_kv, p.N_q, p.N_kv, n_ktiles, xcd_remap, c, p.scale);
   const int n_qtiles = (p.N_q + kQueriesPerWg - 1) / kQueriesPerWg;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_qtiles * p.B * p.H_q)), dim3(kThreads),
                      0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dq, p.H_q,
-                     p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c, p.scale);
+                     p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, p.B * p.H_q, c, p.scale);
   return hipGetLastError();
 }
 

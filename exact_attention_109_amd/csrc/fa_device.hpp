@@ -165,25 +165,42 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint8_t* p0, const uint8_t*
 // Workgroup -> (key/value head index, tile rank). Workgroups are dealt to the
 // 8 XCDs round-robin; when the number of key/value heads allows it, each XCD
 // gets whole key/value heads (all their query heads and tiles) so that K/V
-// is shared through that XCD's L2. Within a head the tile rank runs fastest.
+// is shared through that XCD's L2. Within an XCD the tile rank runs fastest
+// (one head's tiles one after the other), or, with rank_major, slowest: rank
+// 0 of every head of the XCD first, then rank 1, ... -- with tiles ranked
+// heaviest first this deals them in decreasing cost across heads, which keeps
+// the compute units evenly loaded when a unit holds several workgroups and
+// each runs only a few of them.
 struct TileAssign {
   int kvidx, gq, tile_rank;
 };
-__device__ __forceinline__ TileAssign assign_tile(int L, int n_tiles, int G, int xcd_remap) {
+__device__ __forceinline__ TileAssign assign_tile(int L, int n_tiles, int G, int xcd_remap, int n_heads = 0,
+                                                  bool rank_major = false) {
   TileAssign a;
+  int head;  // (key/value head, query head of its group) in order, within the XCD when remapped
   if (xcd_remap) {
     const int xcd = L & 7;
     const int s = L >> 3;
-    a.tile_rank = s % n_tiles;
-    const int head_local = s / n_tiles;
-    a.kvidx = xcd + 8 * (head_local / G);
-    a.gq = head_local % G;
+    const int hpx = n_heads / 8;  // query heads per XCD (n_heads = B * H_q, a multiple of 8 here)
+    if (rank_major) {
+      a.tile_rank = s / hpx;
+      head = s % hpx;
+    } else {
+      a.tile_rank = s % n_tiles;
+      head = s / n_tiles;
+    }
+    a.kvidx = xcd + 8 * (head / G);
   } else {
-    a.tile_rank = L % n_tiles;
-    const int hi = L / n_tiles;
-    a.kvidx = hi / G;
-    a.gq = hi % G;
+    if (rank_major) {
+      a.tile_rank = L / n_heads;
+      head = L % n_heads;
+    } else {
+      a.tile_rank = L % n_tiles;
+      head = L / n_tiles;
+    }
+    a.kvidx = head / G;
   }
+  a.gq = head % G;
   return a;
 }
 
