@@ -47,11 +47,26 @@ class FaError(RuntimeError):
         self.status = status
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa.so (once). Raises if it has not been built."""
+def library_path() -> str:
+    """The library this process loads: libfa.so, or the build named by the
+    FA_LIBRARY environment variable (the check builds of _build.py)."""
+    return os.environ.get("FA_LIBRARY") or LIB_PATH
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the library (once) and declare its entry points. Raises if it has
+    not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path or library_path())
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A separate handle on a build of the library at `path`, with every entry
+    point declared (for comparing builds; the module functions use
+    load_library's)."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
                            " or `python exact_attention_109_amd/_build.py`")
@@ -81,7 +96,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 
@@ -332,7 +346,7 @@ __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_splitkv", "fa_fw
            "fa_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES",
            "fa_fwd_varlen", "fa_fwd_check", "fa_status_string", "fwd", "fwd_splitkv", "fwd_varlen", "fwd_check", "default_num_splits", "bwd", "load_library",
            "FaError", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_DTYPE_F32",
-           "FA_DTYPE_BF16", "LIB_PATH"]
+           "FA_DTYPE_BF16", "LIB_PATH", "library_path", "open_library"]
 
 
 FP8_BLOCK = 128   # rows per descale block

@@ -121,10 +121,15 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, LDS_AS void* ldst) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (loads complete in order, so everything issued before the last N is done).
+// The FA_DEBUG_SYNC build waits for all of them.
 template <int N>
 __device__ __forceinline__ void wait_vmem_keep() {
   static_assert(N >= 0 && N < 16, "vmcnt field");
+#ifdef FA_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+#else
   __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+#endif
 }
 
 // Workgroup barrier without a memory fence. __syncthreads() also waits for
@@ -136,10 +141,19 @@ __device__ __forceinline__ void wait_vmem_keep() {
 // waited for with wait_vmem() by the issuing wave before the barrier that
 // publishes them. The empty asm statements keep the compiler from moving
 // memory accesses across the barrier.
+// The FA_DEBUG_SYNC build (a check, not the product) makes every such
+// barrier a full one: all of the wave's memory operations complete first. The
+// ordering argued above then no longer matters, so any difference between the
+// results of the two builds would expose an LDS race in the fence-free form.
 __device__ __forceinline__ void barrier_nofence() {
+#ifdef FA_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  __syncthreads();
+#else
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+#endif
 }
 
 // Row of a 32-row MFMA A operand that lane m supplies, chosen so that the

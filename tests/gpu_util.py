@@ -25,7 +25,7 @@ TOL = {
 
 
 def ensure_library():
-    if not os.path.exists(fa.LIB_PATH):
+    if not os.path.exists(fa.library_path()):
         from exact_attention_109_amd import _build
         _build.build()
     fa.load_library()
