@@ -110,9 +110,44 @@ def sample_clock_power():
             "gfx_clock_mhz_min": min(clocks), "gfx_clock_mhz_max": max(clocks)}
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0):
-    """Time the fp64 oracle on whole heads of the workload until ~budget_s."""
+def _oracle_heads(w, inp, budget_s: float, backward: bool = False):
+    """Run the oracle on whole heads of workload w (in order) until budget_s
+    has passed or every head is done. Returns (heads, seconds, metric FLOP of
+    those heads): the forward FLOP, or for the backward the 2.5x convention."""
     import oracle
+    G = w.H_q // w.H_kv
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    do = inp.f64("do") if backward else None
+    heads = 0
+    t0 = time.perf_counter()
+    done = False
+    for b in range(w.B):
+        for h in range(w.H_q):
+            if backward:
+                oracle.head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], w.causal, w.scale)
+            else:
+                oracle.head_forward(q[b, h], k[b, h // G], v[b, h // G], w.causal, w.scale)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                done = True
+                break
+        if done:
+            break
+    el = time.perf_counter() - t0
+    per_head = (w.bwd_flop if backward else w.fwd_flop) / (w.B * w.H_q)
+    return heads, el, per_head * heads
+
+
+def _baseline_entry(w, heads, el, flop, what):
+    return {"seconds": round(el, 3), "tflops": flop / el / 1e12, "heads": heads, "of_heads": w.B * w.H_q,
+            "sample": f"{what}: {heads} of {w.B * w.H_q} heads of {w.name} (all {w.N_q} rows each)"}
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0):
+    """The fp64 oracle timed on this host: the bench workload on whole heads
+    for about budget_s (the line's value), then every configuration -- c1 and
+    c2 in full, c4 and the c5 backward on whole heads for a few seconds each --
+    with the host's BLAS threads, and c1 and c2 in full on one core."""
     blas = None
     try:
         from threadpoolctl import threadpool_info
@@ -121,21 +156,8 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
         blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)" for i in info]
     except Exception:
         threads = os.cpu_count() or 1
-    G = w.H_q // w.H_kv
-    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
-    heads = 0
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H_q):
-            oracle.head_forward(q[b, h], k[b, h // G], v[b, h // G], w.causal, w.scale)
-            heads += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    flop = w.fwd_flop / (w.B * w.H_q) * heads
-    return {
+    heads, el, flop = _oracle_heads(w, inp, budget_s)
+    out = {
         "value": flop / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -146,6 +168,30 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
         "os_cpu_count": os.cpu_count(),
         "blas": blas,
     }
+    per = {}
+    for name, budget, backward in (("c1", 1e9, False), ("c2", 1e9, False), ("c4", budget_s * 0.6, False),
+                                   ("c5", budget_s * 0.4, True)):
+        if name not in WORKLOADS or name == w.name:
+            continue
+        wc = WORKLOADS[name]
+        ic = make_inputs(wc)
+        h, e, f = _oracle_heads(wc, ic, budget, backward)
+        per[name] = _baseline_entry(wc, h, e, f, "backward (2.5x FLOP convention)" if backward else "forward")
+        del ic
+    out["per_config"] = per
+    try:
+        from threadpoolctl import threadpool_limits
+        single = {}
+        with threadpool_limits(limits=1):
+            for name in ("c1", "c2"):
+                wc = WORKLOADS[name]
+                ic = make_inputs(wc)
+                h, e, f = _oracle_heads(wc, ic, 1e9)
+                single[name] = _baseline_entry(wc, h, e, f, "forward, one core")
+        out["single_core"] = single
+    except ImportError:
+        out["single_core"] = None
+    return out
 
 
 def time_other_forward(fa, torch, steps: int, main_name: str):
