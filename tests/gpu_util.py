@@ -88,9 +88,9 @@ def o_small_check(got, ref, dtype):
     max-abs <= 1e-2 on every element whose exact value has |O| < 2. Rows of
     one to a few keys can hold |O| in [2, 4), where the output's own bf16
     rounding costs up to 2^-8 = 0.0078 and the bf16 probabilities of the P V
-    product (relative 2^-9 each, not averaged out over so few keys) can add
-    about 0.003 more; those elements are held to 1e-2 + half a bf16 ulp of
-    the exact value. Returns the number of elements that needed that
+    product (unit roundoff 2^-8 each, not averaged out over so few keys) add
+    to it; those elements are held to 1e-2 + half a bf16 ulp of the exact
+    value. Returns the number of elements that needed that
     allowance (0 when the plain bound holds everywhere)."""
     got = np.asarray(got)
     ref = np.asarray(ref)

@@ -46,7 +46,7 @@ def run(inp, k8, kd, v8, vd, causal, scale, S):
 
 def check_head(o, lse, q, k, v, causal, scale):
     """One head against the oracle. O: the bf16 path's bound, scaled to the
-    values: P is rounded to bf16 (2^-9 relative per probability, allowed
+    values: P is rounded to bf16 (2^-8 relative per probability, allowed
     2^-7 here) before the PV product, and O itself is stored in bf16 (half
     an ulp). With the V blocks 2^-3 .. 2^3 apart, a fixed 1e-2 would not
     follow the magnitude of O. LSE: 1e-3 as for bf16."""
