@@ -184,36 +184,41 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const uint8_t* p0, const uint8_t*
 // 0 of every head of the XCD first, then rank 1, ... -- with tiles ranked
 // heaviest first this deals them in decreasing cost across heads, which keeps
 // the compute units evenly loaded when a unit holds several workgroups and
-// each runs only a few of them.
+// each runs only a few of them. With rank_group = g > 1 (and rank_major
+// off) the heads of the XCD are taken g at a time and each group runs rank
+// 0 of its g heads, then rank 1, ...: consecutive workgroups then cost the
+// same. The workgroup dispatcher hands workgroups to an XCD's compute units a
+// few at a time and in order, so a workgroup waits until enough units are
+// free; equal costs let those units free up together (with one head's ranks
+// consecutive, each dispatch waited on the slowest of several unequal
+// tiles). g is reduced to the largest power of two dividing the heads in
+// scope.
 struct TileAssign {
   int kvidx, gq, tile_rank;
 };
 __device__ __forceinline__ TileAssign assign_tile(int L, int n_tiles, int G, int xcd_remap, int n_heads = 0,
-                                                  bool rank_major = false) {
+                                                  bool rank_major = false, int rank_group = 1) {
   TileAssign a;
   int head;  // (key/value head, query head of its group) in order, within the XCD when remapped
-  if (xcd_remap) {
-    const int xcd = L & 7;
-    const int s = L >> 3;
-    const int hpx = n_heads / 8;  // query heads per XCD (n_heads = B * H_q, a multiple of 8 here)
-    if (rank_major) {
-      a.tile_rank = s / hpx;
-      head = s % hpx;
-    } else {
-      a.tile_rank = s % n_tiles;
-      head = s / n_tiles;
-    }
-    a.kvidx = xcd + 8 * (head / G);
+  // s: position within the scope (the XCD when remapped, else the grid);
+  // hs: query heads in that scope (n_heads = B * H_q, a multiple of 8 when remapped)
+  const int s = xcd_remap ? (L >> 3) : L;
+  const int hs = xcd_remap ? n_heads / 8 : n_heads;
+  if (rank_major) {
+    a.tile_rank = s / hs;
+    head = s % hs;
+  } else if (rank_group > 1) {
+    int g = rank_group;
+    while (hs % g) g >>= 1;
+    const int per_group = g * n_tiles;
+    const int r = s % per_group;
+    a.tile_rank = r / g;
+    head = (s / per_group) * g + r % g;
   } else {
-    if (rank_major) {
-      a.tile_rank = L / n_heads;
-      head = L % n_heads;
-    } else {
-      a.tile_rank = L % n_tiles;
-      head = L / n_tiles;
-    }
-    a.kvidx = head / G;
+    a.tile_rank = s % n_tiles;
+    head = s / n_tiles;
   }
+  a.kvidx = xcd_remap ? (L & 7) + 8 * (head / G) : head / G;
   a.gq = head % G;
   return a;
 }

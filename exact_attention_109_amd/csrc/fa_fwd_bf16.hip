@@ -39,8 +39,13 @@
 //    transposes 16-bit elements across lanes.
 //  * Softmax in base 2: scores are multiplied by scale*log2(e) inside one FMA
 //    and exponentiated with v_exp_f32; LSE is converted back with ln 2. The
-//    output rescale is skipped unless some row's max grew by more than 2^8
-//    (exact: the final division and the LSE use the same, possibly stale, max).
+//    running max may be stale by up to 2^8 (exact: the final division and
+//    the LSE use the same max). A block's exponentials are taken against the
+//    running max first and the block max is formed only if some row's block
+//    sum exceeds 2^8 (then the max is raised, O and l rescaled, and the
+//    exponentials taken again); after a block that moved the max, the next
+//    one forms its max first. On the vector ALU, which bounds the loop, this
+//    saves the max of every other block.
 //  * Causal: K/V blocks past the tile's last row are never loaded; masking
 //    runs only on blocks that cross a wave's diagonal or the end of the keys.
 
@@ -123,7 +128,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int G = H_q / H_kv;
 
   // ---- schedule: workgroup -> (batch, head, query tile)
-  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap);
+  // causal tiles differ in cost: deal them rank by rank over groups of four
+  // heads so that consecutive workgroups cost the same
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, (int)(gridDim.x / n_qtiles), false,
+                                    CAUSAL ? 4 : 1);
   const int kvidx = ta.kvidx, gq = ta.gq, tile_rank = ta.tile_rank;
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
@@ -262,6 +270,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // ---- online-softmax state (per query column; l is per lane half)
   float m_run = -INFINITY;
   float l_run = 0.f;
+  bool eager = true;  // form the block max before the exponentials
   f32x16 oacc[C::DSUB];
 #pragma unroll
   for (int s = 0; s < C::DSUB; ++s) oacc[s] = f32x16{};
@@ -341,6 +350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // until the CU's load pipeline accepts it, so a burst of them would stall
   // the wave for the whole transfer instead of overlapping it).
   constexpr int kDmaSlots = 2 * C::DMA_PER_WAVE;
+  auto no_dma = [](int) __attribute__((always_inline)) {};
   constexpr int kSlotsPerStep = kDmaSlots / C::PV_STEPS;
   static_assert(kSlotsPerStep * C::PV_STEPS == kDmaSlots, "DMA slots per exponential step");
   auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
@@ -360,14 +370,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 16; ++i)
           if (32 * n + i > lim) sacc[n][i] = -INFINITY;
     }
-    float mx = sacc[0][0];
+    // Exponentials against the running max. A row's block sum above 2^8
+    // (or inf / NaN: the max was never set) means a probability may exceed
+    // 2^8: the block max is formed, the running max raised and the block's
+    // exponentials taken again. A sum within 2^8 bounds every probability.
+    float psum = 0.f;
+    auto exps = [&](auto&& issue, auto dma_here) __attribute__((always_inline)) {
+      constexpr bool kD = decltype(dma_here)::value;
+      psum = 0.f;
 #pragma unroll
-    for (int n = 0; n < NSUB; ++n)
+      for (int u = 0; u < C::PV_STEPS; ++u) {
+        const int n = u >> 1;
+        const int w8 = (u & 1) * 8;
+        float p[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
-    const float m_blk = max_xor32(mx) * c;
-    if (__any(m_blk > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, m_blk);
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(sacc[n][w8 + e], c, -m_run));
+          psum += p[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+        if constexpr (kD) {
+#pragma unroll
+          for (int r = 0; r < kSlotsPerStep; ++r) issue(u * kSlotsPerStep + r);
+        }
+      }
+      if constexpr (kD) {
+#pragma unroll
+        for (int i = 0; i < kDmaSlots; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgValu, 28 / kSlotsPerStep, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        }
+      }
+    };
+    auto block_max = [&]() __attribute__((always_inline)) {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
+      return max_xor32(mx) * c;
+    };
+    auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -375,34 +419,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
       m_run = m_new;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int u = 0; u < C::PV_STEPS; ++u) {
-      const int n = u >> 1;
-      const int w8 = (u & 1) * 8;
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(sacc[n][w8 + e], c, -m_run));
-        psum += p[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
-      if constexpr (kDma) {
-#pragma unroll
-        for (int r = 0; r < kSlotsPerStep; ++r) issue(u * kSlotsPerStep + r);
+    };
+    bool moved = false;
+    if (eager) {
+      // the previous block moved the max: form this block's max first
+      const float m_blk = block_max();
+      if (__any(m_blk > m_run + kRescaleSlack)) {
+        rescale_to(fmaxf(m_run, m_blk));
+        moved = true;
       }
     }
-    if constexpr (kDma) {
-      // about 28 vector instructions per exponential step (8 x fma, exp,
-      // add; 4 x pack), split evenly between the DMA slots of the step
-#pragma unroll
-      for (int i = 0; i < kDmaSlots; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 28 / kSlotsPerStep, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+    exps(issue, has_dma);
+    if (__any(!(psum <= 256.0f))) {
+      const float m_new = fmaxf(m_run, block_max());
+      // (a sum above 2^8 implies some row's max rose; only NaN inputs can
+      // leave every max unchanged, and then the block stands as computed)
+      if (__any(m_new > m_run)) {
+        rescale_to(m_new);
+        exps(no_dma, std::false_type{});
+        moved = true;
       }
     }
+    eager = moved;
     l_run += psum;
   };
 
@@ -416,7 +454,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // (the group test is outside the loop, so the compiler never has to keep
   // both groups' register state alive across the barriers); both loops pass
   // the same 2*(nblk+1) barriers.
-  auto no_dma = [](int) __attribute__((always_inline)) {};
   auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
     mfma_phase(j, k_cur, v_prev);
     barrier_nofence();
