@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int half = lane >> 5;
   const int G = H_q / H_kv;
 
-  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap);
+  // causal tiles differ in cost: deal them rank by rank over groups of four
+  // heads so that consecutive workgroups cost the same
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, (int)(gridDim.x / n_qtiles), false,
+                                    CAUSAL ? 4 : 1);
   const int kvidx = ta.kvidx, gq = ta.gq, tile_rank = ta.tile_rank;
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
