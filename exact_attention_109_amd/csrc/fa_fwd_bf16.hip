@@ -11,9 +11,14 @@
 // gfx950 mapping
 // --------------
 //  * Workgroup = 8 wave64s, 256 query rows (32 per wave), one workgroup per
-//    CU (2 waves per SIMD). One workgroup per (batch, query head, 256-row
-//    tile); grid order puts the heaviest causal tiles first and keeps all
-//    tiles of one key/value head on one XCD.
+//    CU (2 waves per SIMD). All tiles of one key/value head go to one XCD.
+//    Causal dense calls: a workgroup takes two tiles of one head, r and
+//    n-1-r, one after the other, so that every workgroup costs the same (the
+//    dispatcher starts an XCD's workgroups a few at a time and in order, so
+//    unequal neighbours leave compute units idle) while one head's tiles stay
+//    neighbours in the grid (their K/V is shared through L2). Otherwise one
+//    workgroup per (batch, query head, 256-row tile), causal tiles heaviest
+//    first and dealt rank by rank over groups of four heads.
 //  * Contractions on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The
 //    scores are computed transposed, S^T = K Q^T (K as the A operand, Q as B),
 //    so that a lane owns one query column; P^T then feeds O^T = V^T P^T as the
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE,
     int H_q, int H_kv, int N_q_arg, int N_kv_arg, int n_qtiles, int xcd_remap, float c,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k, int paired) {
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
   constexpr int NSUB = C::NSUB;
@@ -127,17 +132,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int half = lane >> 5;   // lane half: key half for S^T, d half for the Q/K operands
   const int G = H_q / H_kv;
 
-  // ---- schedule: workgroup -> (batch, head, query tile)
-  // causal tiles differ in cost: deal them rank by rank over groups of four
-  // heads so that consecutive workgroups cost the same
-  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, (int)(gridDim.x / n_qtiles), false,
-                                    CAUSAL ? 4 : 1);
+  // ---- schedule: workgroup -> (batch, head, query tile or pair of tiles)
+  // Causal tiles differ in cost. Paired, every workgroup costs the same and
+  // a head's pairs are dealt one after the other; unpaired (packed sequences)
+  // they are dealt rank by rank over groups of four heads, so that
+  // consecutive workgroups still cost about the same.
+  const int n_units = paired ? (n_qtiles + 1) / 2 : n_qtiles;
+  const TileAssign ta = assign_tile(blockIdx.x, n_units, G, xcd_remap, (int)(gridDim.x / n_units), false,
+                                    (CAUSAL && !paired) ? 4 : 1);
   const int kvidx = ta.kvidx, gq = ta.gq, tile_rank = ta.tile_rank;
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
   const int h = hk * G + gq;
-  const int tile = CAUSAL ? (n_qtiles - 1 - tile_rank) : tile_rank;  // heaviest first
-  const int q0 = tile * kBR;
+  const int tile_hi = CAUSAL ? (n_qtiles - 1 - tile_rank) : tile_rank;  // heaviest first
+  const int n_it = (paired && tile_rank != tile_hi) ? 2 : 1;
 
   // Dense: q, o [B][H_q][N_q][D], k, v [B][H_kv][N_kv][D], lse [B][H_q][N_q].
   // Packed sequences (cu_q != null): b is a sequence, q, o [H_q][total_q][D],
@@ -163,364 +171,370 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
     lbase = (size_t(b) * H_q + h) * size_t(N_q);
   }
-  if (q0 >= N_q) return;  // (whole workgroup) a tile past a short sequence
-  if (N_kv == 0) {
-    // a sequence without keys: softmax over nothing; its rows get O = 0 and
-    // LSE = -inf (packed sequences only, dense calls reject N_kv = 0)
-    const int row = q0 + wave * 32 + col;
-    if (row < N_q) {
-      uint16_t* op = O + qbase + size_t(row) * D + half * (D / 2);
+  // tiles of this workgroup: the heavier one first, then (paired) its mirror
+  for (int it = 0; it < n_it; ++it) {
+    const int tile = it == 0 ? tile_hi : tile_rank;
+    const int q0 = tile * kBR;
+    if (it > 0) barrier_nofence();  // every wave is done with the previous tile's LDS
+    if (q0 >= N_q) return;  // (whole workgroup) a tile past a short sequence
+    if (N_kv == 0) {
+      // a sequence without keys: softmax over nothing; its rows get O = 0 and
+      // LSE = -inf (packed sequences only, dense calls reject N_kv = 0)
+      const int row = q0 + wave * 32 + col;
+      if (row < N_q) {
+        uint16_t* op = O + qbase + size_t(row) * D + half * (D / 2);
 #pragma unroll
-      for (int j = 0; j < D / 2; j += 4) st_global8(op + j, u32x2{0u, 0u});
-      if (half == 0) LSE[lbase + row] = -INFINITY;
-    }
-    return;
-  }
-  const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
-  const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
-
-  // ---- Q tile into registers: B operand of S^T = K Q^T (read once)
-  const int wrow0 = q0 + wave * 32;
-  const int qrow = wrow0 + col;
-  bf16x8 qreg[C::QK_STEPS];
-  {
-    const uint16_t* qp = Q + qbase + size_t(min(qrow, N_q - 1)) * D + half * (D / 2);
-#pragma unroll
-    for (int t = 0; t < C::QK_STEPS; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
-  }
-
-  // ---- key blocks visited by the workgroup. Every wave computes all of them:
-  // the phase barriers make a block cost the same time whether or not a wave
-  // skips it, and a block entirely past a wave's rows is masked to exact
-  // zeros (every row sees key 0 in block 0, so its running max is finite
-  // from then on and exp2 of a masked score is 0).
-  const int nblk_all = (N_kv + BC - 1) / BC;
-  int nblk = nblk_all;
-  if (CAUSAL) {
-    const int last_row = min(q0 + kBR, N_q) - 1;
-    nblk = min(nblk_all, last_row / BC + 1);
-  }
-  auto need_mask = [&](int j) __attribute__((always_inline)) {
-    const int kv0 = j * BC;
-    return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
-  };
-
-  // ---- LDS-DMA staging by the 4 waves of group B: each fills DMA_PER_WAVE
-  // KiB of a tile. Instruction i writes bytes [1024*ig, 1024*ig + 1024) of the
-  // tile, lane l the 16 bytes at 16*l: row RPI*ig + l/CPR, physical chunk
-  // l%CPR, which holds logical chunk (l%CPR) ^ swz(row).
-  // The *_t offsets serve the last key block when N_kv is not a multiple of
-  // BC: they read row min(row, last valid row) instead (finite data for the
-  // masked keys, and no access past the end of K and V).
-  const int tail_blk = (N_kv % BC) ? N_kv / BC : -1;
-  const int tail_lim = N_kv - 1 - (N_kv / BC) * BC;
-  uint32_t dma_koff[C::DMA_PER_WAVE], dma_voff[C::DMA_PER_WAVE];
-  uint32_t dma_koff_t[C::DMA_PER_WAVE], dma_voff_t[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-    const int ig = gw * C::DMA_PER_WAVE + i;
-    const int row = C::RPI * ig + lane / C::CPR;
-    const int p = lane % C::CPR;
-    const int cut = (row - min(row, tail_lim)) * C::ROW_BYTES;
-    dma_koff[i] = row * C::ROW_BYTES + (p ^ swz_k<D>(row)) * 16;
-    dma_voff[i] = row * C::ROW_BYTES + (p ^ swz_v<D>(row)) * 16;
-    dma_koff_t[i] = dma_koff[i] - cut;
-    dma_voff_t[i] = dma_voff[i] - cut;
-  }
-  // DMA slot i of a vector phase of group B: slots 0 .. DMA_PER_WAVE-1 stage
-  // 1 KiB pieces of the K tile at key block jk, the others pieces of the V
-  // tile at block jv, each from a uniform base plus a per-lane 32-bit offset
-  // (the clamped one for block tail_blk, picked by a uniform select).
-  auto dma_slot = [&](int i, int jk, int jv, uint8_t* kdst, uint8_t* vdst)
-      __attribute__((always_inline)) {
-    const bool is_k = i < C::DMA_PER_WAVE;
-    const int ii = is_k ? i : i - C::DMA_PER_WAVE;
-    const int jb = is_k ? jk : jv;
-    const uint8_t* src = (is_k ? Kbytes : Vbytes) + size_t(jb) * BC * C::ROW_BYTES;
-    uint32_t off = is_k ? dma_koff[ii] : dma_voff[ii];
-    if (jb == tail_blk) off = is_k ? dma_koff_t[ii] : dma_voff_t[ii];
-    lds_dma16_sbase(src, off, lds_address(is_k ? kdst : vdst) + 1024 * (gw * C::DMA_PER_WAVE + ii));
-  };
-  // K_0 for the prologue (only group B calls it)
-  auto dma_k0 = [&](uint8_t* kdst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_slot(i, 0, 0, kdst, kdst);
-  };
-
-  // ---- per-lane LDS read offsets (bytes within a tile)
-  // K (S^T A operand): row row_of_lane(col) of subtile n (n adds 32 rows), chunk (D/16)*half + t.
-  const int krow = row_of_lane(col);
-  int koff[C::QK_STEPS];
-#pragma unroll
-  for (int t = 0; t < C::QK_STEPS; ++t)
-    koff[t] = krow * C::ROW_BYTES + ((((D / 16) * half + t) ^ swz_k<D>(krow)) * 16);
-  // V (O^T A operand via transposed reads): a 16-lane group j = lane%16 reads
-  // rows r0 + j/4 (r0 = 32n + 16*half + 8w + 4r) at columns c0 + 4*(j%4),
-  // c0 = 32*s + 16*((lane%32)/16).
-  const int j16 = lane & 15;
-  const int vgrp = (lane & 31) >> 4;
-  int voff[C::DSUB];
-#pragma unroll
-  for (int s = 0; s < C::DSUB; ++s) {
-    const int row = 16 * half + (j16 >> 2);
-    const int cc = 32 * s + 16 * vgrp + 4 * (j16 & 3);
-    voff[s] = row * C::ROW_BYTES + (((cc >> 3) ^ swz_v<D>(row)) * 16) + (cc & 7) * 2;
-  }
-
-  // ---- online-softmax state (per query column; l is per lane half)
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  bool eager = true;  // form the block max before the exponentials
-  f32x16 oacc[C::DSUB];
-#pragma unroll
-  for (int s = 0; s < C::DSUB; ++s) oacc[s] = f32x16{};
-  f32x16 sacc[NSUB];          // scores of the current block
-  u32x4 pk[C::PV_STEPS];      // its probabilities, bf16-packed as PV B operands
-
-  // MFMA phase for block j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
-  auto pv_part = [&](const uint8_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < C::PV_STEPS; ++u) {
-      const int rbase = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;  // + 4 rows for the second read
-#pragma unroll
-      for (int s = 0; s < C::DSUB; ++s) {
-        LDS_AS i16x4* p0 = (LDS_AS i16x4*)(vt + voff[s] + rbase);
-        LDS_AS i16x4* p1 = (LDS_AS i16x4*)(vt + voff[s] + rbase + 4 * C::ROW_BYTES);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
-        u32x4 av;
-        av[0] = __builtin_bit_cast(u32x2, lo)[0];
-        av[1] = __builtin_bit_cast(u32x2, lo)[1];
-        av[2] = __builtin_bit_cast(u32x2, hi)[0];
-        av[3] = __builtin_bit_cast(u32x2, hi)[1];
-        oacc[s] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pk[u]), oacc[s]);
+        for (int j = 0; j < D / 2; j += 4) st_global8(op + j, u32x2{0u, 0u});
+        if (half == 0) LSE[lbase + row] = -INFINITY;
       }
+      return;
     }
-  };
-  auto qk_part = [&](const uint8_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int n = 0; n < NSUB; ++n) sacc[n] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::QK_STEPS; ++t) {
-#pragma unroll
-      for (int n = 0; n < NSUB; ++n) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[t] + n * 32 * C::ROW_BYTES));
-        sacc[n] = mfma32x32x16(a, qreg[t], sacc[n]);
-      }
-    }
-  };
-  // Operand reads run ahead of the MFMAs that consume them: 8 V reads up
-  // front, then 2 reads behind every PV MFMA and 1 behind every QK^T MFMA
-  // (the K reads of the QK^T part start while the last PV MFMAs run).
-  auto pv_schedule = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-#pragma unroll
-    for (int i = 0; i < C::PV_STEPS * C::DSUB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    }
-  };
-  auto qk_schedule = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::QK_STEPS * NSUB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    }
-  };
-  auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-    const bool do_pv = j >= 1;
-    const bool do_qk = j < nblk;
-    if (do_pv) {
-      pv_part(vt);
-      pv_schedule();
-    }
-    if (do_qk) {
-      qk_part(kt);
-#pragma unroll
-      for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      qk_schedule();
-    }
-  };
+    const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
+    const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
 
-  // Vector phase for block j: mask, block max, (rare) rescale, exponentials,
-  // row sums and bf16 packing. `issue(i)`, i = 0 .. kDmaSlots-1, issues the
-  // LDS-DMA instructions of the loading group; they are spread through the
-  // exponential loop (a wave that issues a vector-memory instruction stalls
-  // until the CU's load pipeline accepts it, so a burst of them would stall
-  // the wave for the whole transfer instead of overlapping it).
-  constexpr int kDmaSlots = 2 * C::DMA_PER_WAVE;
-  auto no_dma = [](int) __attribute__((always_inline)) {};
-  constexpr int kSlotsPerStep = kDmaSlots / C::PV_STEPS;
-  static_assert(kSlotsPerStep * C::PV_STEPS == kDmaSlots, "DMA slots per exponential step");
-  auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
-    constexpr bool kDma = decltype(has_dma)::value;
-    if constexpr (!kDma) {
-      if (j >= nblk) return;  // the step that only finishes PV of the last block
-    }
-    if (need_mask(j)) {
-      // key kv0 + 32n + 16*half + i is visible iff it is <= last_key (the
-      // row itself when causal, and < N_kv); one compare against the
-      // register's constant key offset per score.
-      const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
-      const int lim = last_key - j * BC - 16 * half;
-#pragma unroll
-      for (int n = 0; n < NSUB; ++n)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * n + i > lim) sacc[n][i] = -INFINITY;
-    }
-    // Exponentials against the running max. A row's block sum above 2^8
-    // (or inf / NaN: the max was never set) means a probability may exceed
-    // 2^8: the block max is formed, the running max raised and the block's
-    // exponentials taken again. A sum within 2^8 bounds every probability.
-    float psum = 0.f;
-    auto exps = [&](auto&& issue, auto dma_here) __attribute__((always_inline)) {
-      constexpr bool kD = decltype(dma_here)::value;
-      psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < C::PV_STEPS; ++u) {
-        const int n = u >> 1;
-        const int w8 = (u & 1) * 8;
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(sacc[n][w8 + e], c, -m_run));
-          psum += p[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
-        if constexpr (kD) {
-#pragma unroll
-          for (int r = 0; r < kSlotsPerStep; ++r) issue(u * kSlotsPerStep + r);
-        }
-      }
-      if constexpr (kD) {
-#pragma unroll
-        for (int i = 0; i < kDmaSlots; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSgValu, 28 / kSlotsPerStep, 0);
-          __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
-        }
-      }
-    };
-    auto block_max = [&]() __attribute__((always_inline)) {
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int n = 0; n < NSUB; ++n)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
-      return max_xor32(mx) * c;
-    };
-    auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int s = 0; s < C::DSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
-      m_run = m_new;
-    };
-    bool moved = false;
-    if (eager) {
-      // the previous block moved the max: form this block's max first
-      const float m_blk = block_max();
-      if (__any(m_blk > m_run + kRescaleSlack)) {
-        rescale_to(fmaxf(m_run, m_blk));
-        moved = true;
-      }
-    }
-    exps(issue, has_dma);
-    if (__any(!(psum <= 256.0f))) {
-      const float m_new = fmaxf(m_run, block_max());
-      // (a sum above 2^8 implies some row's max rose; only NaN inputs can
-      // leave every max unchanged, and then the block stands as computed)
-      if (__any(m_new > m_run)) {
-        rescale_to(m_new);
-        exps(no_dma, std::false_type{});
-        moved = true;
-      }
-    }
-    eager = moved;
-    l_run += psum;
-  };
-
-  // Two phases (ticks) per block j. Group A: MFMA(j) | VALU(j).
-  // Group B: VALU(j-1) + DMA of K_{j+1}, V_j | MFMA(j), then wait for the DMA.
-  // The phase barriers carry no memory fence: every LDS read of a phase is
-  // consumed by an MFMA of the same phase, so a buffer is free for the next
-  // DMA once the barrier after its last reading phase has passed, and DMA
-  // data is waited for explicitly one phase after it was issued.
-  // Buffers: K_j in kb[j%2], V_j in vb[j%2]. Each group runs its own loop
-  // (the group test is outside the loop, so the compiler never has to keep
-  // both groups' register state alive across the barriers); both loops pass
-  // the same 2*(nblk+1) barriers.
-  auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
-    mfma_phase(j, k_cur, v_prev);
-    barrier_nofence();
-    valu_phase(j, no_dma, std::false_type{});
-    barrier_nofence();
-  };
-  auto block_b = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev, uint8_t* k_dma, uint8_t* v_dma)
-      __attribute__((always_inline)) {
-    // K_{j+1} and V_j; past the last block the last one is loaded again into
-    // a buffer nobody reads any more, which keeps the issue slots unconditional.
-    const int jk = min(j + 1, nblk - 1);
-    const int jv = min(j, nblk - 1);
-    valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
-      dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
-    barrier_nofence();  // the DMA stays in flight through the next phase
-    mfma_phase(j, k_cur, v_prev);
-    wait_vmem();        // K_{j+1} and V_j are in LDS before the barrier publishes them
-    barrier_nofence();
-  };
-
-  // ---- prologue: K_0 into kb0
-  if (grp == 1) {
-    dma_k0(kb0);
-    wait_vmem();
-  }
-  __syncthreads();
-
-  // Blocks 0..nblk: the extra step j = nblk finishes PV of the last block.
-  if (grp == 0) {
-    for (int j = 0; j <= nblk; j += 2) {
-      block_a(j, kb0, vb1);
-      if (j + 1 <= nblk) block_a(j + 1, kb1, vb0);
-    }
-  } else {
-    // Step 0 has no softmax yet: only the loads of K_1 and V_0, then QK^T of
-    // block 0 (peeled, so that every vector phase in the loop has work).
+    // ---- Q tile into registers: B operand of S^T = K Q^T (read once)
+    const int wrow0 = q0 + wave * 32;
+    const int qrow = wrow0 + col;
+    bf16x8 qreg[C::QK_STEPS];
     {
-      const int jk = min(1, nblk - 1);
+      const uint16_t* qp = Q + qbase + size_t(min(qrow, N_q - 1)) * D + half * (D / 2);
 #pragma unroll
-      for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, 0, kb1, vb0);
-      barrier_nofence();
-      mfma_phase(0, kb0, vb1);
-      wait_vmem();
-      barrier_nofence();
+      for (int t = 0; t < C::QK_STEPS; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
     }
-    for (int j = 1; j <= nblk; j += 2) {
-      block_b(j, kb1, vb0, kb0, vb1);
-      if (j + 1 <= nblk) block_b(j + 1, kb0, vb1, kb1, vb0);
-    }
-  }
 
-  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
-  const float l_tot = sum_xor32(l_run);
-  if (qrow < N_q) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = O + qbase + size_t(qrow) * D;
+    // ---- key blocks visited by the workgroup. Every wave computes all of them:
+    // the phase barriers make a block cost the same time whether or not a wave
+    // skips it, and a block entirely past a wave's rows is masked to exact
+    // zeros (every row sees key 0 in block 0, so its running max is finite
+    // from then on and exp2 of a masked score is 0).
+    const int nblk_all = (N_kv + BC - 1) / BC;
+    int nblk = nblk_all;
+    if (CAUSAL) {
+      const int last_row = min(q0 + kBR, N_q) - 1;
+      nblk = min(nblk_all, last_row / BC + 1);
+    }
+    auto need_mask = [&](int j) __attribute__((always_inline)) {
+      const int kv0 = j * BC;
+      return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
+    };
+
+    // ---- LDS-DMA staging by the 4 waves of group B: each fills DMA_PER_WAVE
+    // KiB of a tile. Instruction i writes bytes [1024*ig, 1024*ig + 1024) of the
+    // tile, lane l the 16 bytes at 16*l: row RPI*ig + l/CPR, physical chunk
+    // l%CPR, which holds logical chunk (l%CPR) ^ swz(row).
+    // The *_t offsets serve the last key block when N_kv is not a multiple of
+    // BC: they read row min(row, last valid row) instead (finite data for the
+    // masked keys, and no access past the end of K and V).
+    const int tail_blk = (N_kv % BC) ? N_kv / BC : -1;
+    const int tail_lim = N_kv - 1 - (N_kv / BC) * BC;
+    uint32_t dma_koff[C::DMA_PER_WAVE], dma_voff[C::DMA_PER_WAVE];
+    uint32_t dma_koff_t[C::DMA_PER_WAVE], dma_voff_t[C::DMA_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int ig = gw * C::DMA_PER_WAVE + i;
+      const int row = C::RPI * ig + lane / C::CPR;
+      const int p = lane % C::CPR;
+      const int cut = (row - min(row, tail_lim)) * C::ROW_BYTES;
+      dma_koff[i] = row * C::ROW_BYTES + (p ^ swz_k<D>(row)) * 16;
+      dma_voff[i] = row * C::ROW_BYTES + (p ^ swz_v<D>(row)) * 16;
+      dma_koff_t[i] = dma_koff[i] - cut;
+      dma_voff_t[i] = dma_voff[i] - cut;
+    }
+    // DMA slot i of a vector phase of group B: slots 0 .. DMA_PER_WAVE-1 stage
+    // 1 KiB pieces of the K tile at key block jk, the others pieces of the V
+    // tile at block jv, each from a uniform base plus a per-lane 32-bit offset
+    // (the clamped one for block tail_blk, picked by a uniform select).
+    auto dma_slot = [&](int i, int jk, int jv, uint8_t* kdst, uint8_t* vdst)
+        __attribute__((always_inline)) {
+      const bool is_k = i < C::DMA_PER_WAVE;
+      const int ii = is_k ? i : i - C::DMA_PER_WAVE;
+      const int jb = is_k ? jk : jv;
+      const uint8_t* src = (is_k ? Kbytes : Vbytes) + size_t(jb) * BC * C::ROW_BYTES;
+      uint32_t off = is_k ? dma_koff[ii] : dma_voff[ii];
+      if (jb == tail_blk) off = is_k ? dma_koff_t[ii] : dma_voff_t[ii];
+      lds_dma16_sbase(src, off, lds_address(is_k ? kdst : vdst) + 1024 * (gw * C::DMA_PER_WAVE + ii));
+    };
+    // K_0 for the prologue (only group B calls it)
+    auto dma_k0 = [&](uint8_t* kdst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_slot(i, 0, 0, kdst, kdst);
+    };
+
+    // ---- per-lane LDS read offsets (bytes within a tile)
+    // K (S^T A operand): row row_of_lane(col) of subtile n (n adds 32 rows), chunk (D/16)*half + t.
+    const int krow = row_of_lane(col);
+    int koff[C::QK_STEPS];
+#pragma unroll
+    for (int t = 0; t < C::QK_STEPS; ++t)
+      koff[t] = krow * C::ROW_BYTES + ((((D / 16) * half + t) ^ swz_k<D>(krow)) * 16);
+    // V (O^T A operand via transposed reads): a 16-lane group j = lane%16 reads
+    // rows r0 + j/4 (r0 = 32n + 16*half + 8w + 4r) at columns c0 + 4*(j%4),
+    // c0 = 32*s + 16*((lane%32)/16).
+    const int j16 = lane & 15;
+    const int vgrp = (lane & 31) >> 4;
+    int voff[C::DSUB];
 #pragma unroll
     for (int s = 0; s < C::DSUB; ++s) {
+      const int row = 16 * half + (j16 >> 2);
+      const int cc = 32 * s + 16 * vgrp + 4 * (j16 & 3);
+      voff[s] = row * C::ROW_BYTES + (((cc >> 3) ^ swz_v<D>(row)) * 16) + (cc & 7) * 2;
+    }
+
+    // ---- online-softmax state (per query column; l is per lane half)
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    bool eager = true;  // form the block max before the exponentials
+    f32x16 oacc[C::DSUB];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 w;
-        w[0] = cvt_pk_bf16(oacc[s][4 * a + 0] * inv, oacc[s][4 * a + 1] * inv);
-        w[1] = cvt_pk_bf16(oacc[s][4 * a + 2] * inv, oacc[s][4 * a + 3] * inv);
-        st_global8(op + 32 * s + 8 * a + 4 * half, w);
+    for (int s = 0; s < C::DSUB; ++s) oacc[s] = f32x16{};
+    f32x16 sacc[NSUB];          // scores of the current block
+    u32x4 pk[C::PV_STEPS];      // its probabilities, bf16-packed as PV B operands
+
+    // MFMA phase for block j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
+    auto pv_part = [&](const uint8_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < C::PV_STEPS; ++u) {
+        const int rbase = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;  // + 4 rows for the second read
+#pragma unroll
+        for (int s = 0; s < C::DSUB; ++s) {
+          LDS_AS i16x4* p0 = (LDS_AS i16x4*)(vt + voff[s] + rbase);
+          LDS_AS i16x4* p1 = (LDS_AS i16x4*)(vt + voff[s] + rbase + 4 * C::ROW_BYTES);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+          u32x4 av;
+          av[0] = __builtin_bit_cast(u32x2, lo)[0];
+          av[1] = __builtin_bit_cast(u32x2, lo)[1];
+          av[2] = __builtin_bit_cast(u32x2, hi)[0];
+          av[3] = __builtin_bit_cast(u32x2, hi)[1];
+          oacc[s] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pk[u]), oacc[s]);
+        }
+      }
+    };
+    auto qk_part = [&](const uint8_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n) sacc[n] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::QK_STEPS; ++t) {
+#pragma unroll
+        for (int n = 0; n < NSUB; ++n) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[t] + n * 32 * C::ROW_BYTES));
+          sacc[n] = mfma32x32x16(a, qreg[t], sacc[n]);
+        }
+      }
+    };
+    // Operand reads run ahead of the MFMAs that consume them: 8 V reads up
+    // front, then 2 reads behind every PV MFMA and 1 behind every QK^T MFMA
+    // (the K reads of the QK^T part start while the last PV MFMAs run).
+    auto pv_schedule = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+#pragma unroll
+      for (int i = 0; i < C::PV_STEPS * C::DSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      }
+    };
+    auto qk_schedule = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < C::QK_STEPS * NSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      }
+    };
+    auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+      const bool do_pv = j >= 1;
+      const bool do_qk = j < nblk;
+      if (do_pv) {
+        pv_part(vt);
+        pv_schedule();
+      }
+      if (do_qk) {
+        qk_part(kt);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        qk_schedule();
+      }
+    };
+
+    // Vector phase for block j: mask, block max, (rare) rescale, exponentials,
+    // row sums and bf16 packing. `issue(i)`, i = 0 .. kDmaSlots-1, issues the
+    // LDS-DMA instructions of the loading group; they are spread through the
+    // exponential loop (a wave that issues a vector-memory instruction stalls
+    // until the CU's load pipeline accepts it, so a burst of them would stall
+    // the wave for the whole transfer instead of overlapping it).
+    constexpr int kDmaSlots = 2 * C::DMA_PER_WAVE;
+    auto no_dma = [](int) __attribute__((always_inline)) {};
+    constexpr int kSlotsPerStep = kDmaSlots / C::PV_STEPS;
+    static_assert(kSlotsPerStep * C::PV_STEPS == kDmaSlots, "DMA slots per exponential step");
+    auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
+      constexpr bool kDma = decltype(has_dma)::value;
+      if constexpr (!kDma) {
+        if (j >= nblk) return;  // the step that only finishes PV of the last block
+      }
+      if (need_mask(j)) {
+        // key kv0 + 32n + 16*half + i is visible iff it is <= last_key (the
+        // row itself when causal, and < N_kv); one compare against the
+        // register's constant key offset per score.
+        const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
+        const int lim = last_key - j * BC - 16 * half;
+#pragma unroll
+        for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * n + i > lim) sacc[n][i] = -INFINITY;
+      }
+      // Exponentials against the running max. A row's block sum above 2^8
+      // (or inf / NaN: the max was never set) means a probability may exceed
+      // 2^8: the block max is formed, the running max raised and the block's
+      // exponentials taken again. A sum within 2^8 bounds every probability.
+      float psum = 0.f;
+      auto exps = [&](auto&& issue, auto dma_here) __attribute__((always_inline)) {
+        constexpr bool kD = decltype(dma_here)::value;
+        psum = 0.f;
+#pragma unroll
+        for (int u = 0; u < C::PV_STEPS; ++u) {
+          const int n = u >> 1;
+          const int w8 = (u & 1) * 8;
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(fmaf(sacc[n][w8 + e], c, -m_run));
+            psum += p[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[u][e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+          if constexpr (kD) {
+#pragma unroll
+            for (int r = 0; r < kSlotsPerStep; ++r) issue(u * kSlotsPerStep + r);
+          }
+        }
+        if constexpr (kD) {
+#pragma unroll
+          for (int i = 0; i < kDmaSlots; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 28 / kSlotsPerStep, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+          }
+        }
+      };
+      auto block_max = [&]() __attribute__((always_inline)) {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
+        return max_xor32(mx) * c;
+      };
+      auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int s = 0; s < C::DSUB; ++s)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
+        m_run = m_new;
+      };
+      bool moved = false;
+      if (eager) {
+        // the previous block moved the max: form this block's max first
+        const float m_blk = block_max();
+        if (__any(m_blk > m_run + kRescaleSlack)) {
+          rescale_to(fmaxf(m_run, m_blk));
+          moved = true;
+        }
+      }
+      exps(issue, has_dma);
+      if (__any(!(psum <= 256.0f))) {
+        const float m_new = fmaxf(m_run, block_max());
+        // (a sum above 2^8 implies some row's max rose; only NaN inputs can
+        // leave every max unchanged, and then the block stands as computed)
+        if (__any(m_new > m_run)) {
+          rescale_to(m_new);
+          exps(no_dma, std::false_type{});
+          moved = true;
+        }
+      }
+      eager = moved;
+      l_run += psum;
+    };
+
+    // Two phases (ticks) per block j. Group A: MFMA(j) | VALU(j).
+    // Group B: VALU(j-1) + DMA of K_{j+1}, V_j | MFMA(j), then wait for the DMA.
+    // The phase barriers carry no memory fence: every LDS read of a phase is
+    // consumed by an MFMA of the same phase, so a buffer is free for the next
+    // DMA once the barrier after its last reading phase has passed, and DMA
+    // data is waited for explicitly one phase after it was issued.
+    // Buffers: K_j in kb[j%2], V_j in vb[j%2]. Each group runs its own loop
+    // (the group test is outside the loop, so the compiler never has to keep
+    // both groups' register state alive across the barriers); both loops pass
+    // the same 2*(nblk+1) barriers.
+    auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
+      mfma_phase(j, k_cur, v_prev);
+      barrier_nofence();
+      valu_phase(j, no_dma, std::false_type{});
+      barrier_nofence();
+    };
+    auto block_b = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev, uint8_t* k_dma, uint8_t* v_dma)
+        __attribute__((always_inline)) {
+      // K_{j+1} and V_j; past the last block the last one is loaded again into
+      // a buffer nobody reads any more, which keeps the issue slots unconditional.
+      const int jk = min(j + 1, nblk - 1);
+      const int jv = min(j, nblk - 1);
+      valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
+        dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
+      barrier_nofence();  // the DMA stays in flight through the next phase
+      mfma_phase(j, k_cur, v_prev);
+      wait_vmem();        // K_{j+1} and V_j are in LDS before the barrier publishes them
+      barrier_nofence();
+    };
+
+    // ---- prologue: K_0 into kb0
+    if (grp == 1) {
+      dma_k0(kb0);
+      wait_vmem();
+    }
+    __syncthreads();
+
+    // Blocks 0..nblk: the extra step j = nblk finishes PV of the last block.
+    if (grp == 0) {
+      for (int j = 0; j <= nblk; j += 2) {
+        block_a(j, kb0, vb1);
+        if (j + 1 <= nblk) block_a(j + 1, kb1, vb0);
+      }
+    } else {
+      // Step 0 has no softmax yet: only the loads of K_1 and V_0, then QK^T of
+      // block 0 (peeled, so that every vector phase in the loop has work).
+      {
+        const int jk = min(1, nblk - 1);
+#pragma unroll
+        for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, 0, kb1, vb0);
+        barrier_nofence();
+        mfma_phase(0, kb0, vb1);
+        wait_vmem();
+        barrier_nofence();
+      }
+      for (int j = 1; j <= nblk; j += 2) {
+        block_b(j, kb1, vb0, kb0, vb1);
+        if (j + 1 <= nblk) block_b(j + 1, kb0, vb1, kb1, vb0);
       }
     }
-    if (half == 0) LSE[lbase + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+
+    // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+    const float l_tot = sum_xor32(l_run);
+    if (qrow < N_q) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* op = O + qbase + size_t(qrow) * D;
+#pragma unroll
+      for (int s = 0; s < C::DSUB; ++s) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 w;
+          w[0] = cvt_pk_bf16(oacc[s][4 * a + 0] * inv, oacc[s][4 * a + 1] * inv);
+          w[1] = cvt_pk_bf16(oacc[s][4 * a + 2] * inv, oacc[s][4 * a + 3] * inv);
+          st_global8(op + 32 * s + 8 * a + 4 * half, w);
+        }
+      }
+      if (half == 0) LSE[lbase + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -529,7 +543,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream) {
   const int n_qtiles = (p.N_q + kBR - 1) / kBR;
-  const long long nwg = (long long)n_qtiles * p.B * p.H_q;
+  const int paired = (CAUSAL && vl == nullptr) ? 1 : 0;
+  const long long nwg = (long long)(paired ? (n_qtiles + 1) / 2 : n_qtiles) * p.B * p.H_q;
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
   // Masked scores are -inf and exp2(-inf * c) must be 0, so c stays positive:
   // for scale == 0 the smallest normal float gives exactly the uniform weights
@@ -540,7 +555,7 @@ hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream
                      static_cast<const uint16_t*>(p.v), static_cast<uint16_t*>(p.o), p.lse,
                      p.H_q, p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c,
                      vl ? vl->cu_q : nullptr, vl ? vl->cu_k : nullptr, vl ? vl->total_q : 0,
-                     vl ? vl->total_k : 0);
+                     vl ? vl->total_k : 0, paired);
   return hipGetLastError();
 }
 
