@@ -357,6 +357,10 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
           for (int e = 0; e < 4; ++e) pk[2 * n + w][e] = cvt_pk_bf16(sx[n][8 * w + 2 * e], sx[n][8 * w + 2 * e + 1]);
       }
+      // P(j) is packed in this tick: left alone, the compiler sinks the
+      // packing past the barrier into the dV MFMAs of the next one
+#pragma unroll
+      for (int u = 0; u < C::STEPS; ++u) asm volatile("" : "+v"(pk[u]));
       wait_lds();          // P(j) is in LDS before the barrier hands it over
       barrier_nofence();
       // tick 2: dV += dO(j)^T P(j)
@@ -416,6 +420,9 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
           for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(px[n][8 * w + 2 * e], px[n][8 * w + 2 * e + 1]);
       }
+      // dS(j) is formed in this tick, beside the partner's dV MFMAs
+#pragma unroll
+      for (int u = 0; u < C::STEPS; ++u) asm volatile("" : "+v"(sk[u]));
 #pragma unroll
       for (int slot = 4 * C::NSUB; slot < 2 * DPW; ++slot) dma_slot(slot, jd, BFP);
       if (pw < 2) {
