@@ -468,46 +468,49 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-constexpr int kQueriesPerWg = 128;  // 4 waves x 32 queries
+// dQ with two wave groups per workgroup in opposite phases (as the forward):
+// 8 waves, 256 queries (32 per wave); waves w and w + 4 share a SIMD. Per key
+// block j each wave runs an MFMA phase -- Z(j-1): dQ^T += K_{j-1}^T dS^T_{j-1},
+// then X(j): S^T = K_j Q^T, dP^T = V_j dO^T -- and a vector phase Y(j): P,
+// dS^T = P (dP - D), packed. Group B runs one phase behind group A, with a
+// workgroup barrier at every phase boundary, so on each SIMD one wave drives
+// the matrix core while the other does its vector work. Group B also loads
+// the K/V block j+1 during its vector phase of block j into a 3-deep ring
+// (block j-1 is still read by Z in block j) and waits for it at the end of
+// its MFMA phase. (Two independent 4-wave workgroups per compute unit, whose
+// phases drift freely, measured 1-3 % slower.)
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;  // queries per workgroup
+constexpr int kDqRing = 3;
 
-// Per wave (32 queries) and streamed key block j (64 keys):
-//   X(j): S^T = K Q^T, dP^T = V dO^T          (MFMA, K/V rows from LDS)
-//   Y(j): P, dS^T = P (dP - D), packed         (VALU)
-//   Z(j): dQ^T += K^T dS^T                     (MFMA, K read transposed)
-// in that order, with the LDS-DMA of block j+1 into the other buffer issued
-// between the vector work of Y(j). Overlap of MFMA and vector work comes from
-// the second workgroup on the compute unit (two waves per SIMD): within one
-// wave the two barely overlap on this hardware, and the software-pipelined
-// form that needs S/dP twice (420 registers, one wave per SIMD) measured
-// 2-3 % slower.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     float* __restrict__ dQ, int H_q, int H_kv, int N_q, int N_kv, int n_qtiles, int xcd_remap, int B_heads,
     float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int BK = C::BLK;
-  constexpr int DPW = C::DMA_PER_WAVE;
-  constexpr int kNB = 2;  // two workgroups per CU: 64 KiB of LDS each
-  __shared__ __attribute__((aligned(1024))) uint8_t ks[kNB][C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs[kNB][C::TILE_BYTES];
+  constexpr int DPW = C::DMA_PER_WAVE;  // 1 KiB pieces per loader wave (4 loaders) and tile
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[kDqRing][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[kDqRing][C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: group A (leads), 1: group B (one phase behind, loads K/V)
+  const int gw = wave & 3;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int G = H_q / H_kv;
 
-  // two workgroups per compute unit and few tiles each: deal them heaviest
-  // first across all heads (rank-major)
   const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, B_heads, true);
   const int b = ta.kvidx / H_kv;
   const int hk = ta.kvidx % H_kv;
   const int h = hk * G + ta.gq;
   const int tile = CAUSAL ? (n_qtiles - 1 - ta.tile_rank) : ta.tile_rank;  // heaviest first
-  const int q0 = tile * kQueriesPerWg;
+  const int q0 = tile * kDqRows;
   const int wq0 = q0 + 32 * wave;
   const int query = wq0 + col;  // this lane's query (MFMA column)
 
@@ -528,17 +531,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
 
   // key blocks of the workgroup; every wave runs all of them (blocks past a
-  // wave's queries are masked to zero).
+  // wave's queries are masked to zero)
   const int nblk_all = (N_kv + BK - 1) / BK;
   int nblk = nblk_all;
-  if (CAUSAL) nblk = min(nblk_all, (min(q0 + kQueriesPerWg, N_q) - 1) / BK + 1);
+  if (CAUSAL) nblk = min(nblk_all, (min(q0 + kDqRows, N_q) - 1) / BK + 1);
 
   const int tail_blk = (N_kv % BK) ? N_kv / BK : -1;
   const int tail_lim = (N_kv - 1) % BK;
   uint32_t doff[DPW], doff_t[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
-    const int ig = wave * DPW + i;
+    const int ig = gw * DPW + i;
     const int row = C::RPI * ig + lane / C::CPR;
     const int pch = lane % C::CPR;
     doff[i] = row * C::ROW_BYTES + (pch ^ swz<D>(row)) * 16;
@@ -547,12 +550,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + kvbase);
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + kvbase);
   constexpr int kSlots = 2 * DPW;
-  auto dma_slot = [&](int i, int j, int bf) __attribute__((always_inline)) {
+  auto dma_slot = [&](int i, int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const bool is_k = i < DPW;
     const int ii = is_k ? i : i - DPW;
     const uint8_t* src = (is_k ? Kb : Vb) + size_t(j) * BK * C::ROW_BYTES;
     lds_dma16_sbase_nc(src, j == tail_blk ? doff_t[ii] : doff[ii],
-                       lds_address(is_k ? ks[bf] : vs[bf]) + 1024 * (wave * DPW + ii));
+                       lds_address(is_k ? kdst : vdst) + 1024 * (gw * DPW + ii));
   };
 
   ReadOffsets<D> ro;
@@ -565,9 +568,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x4 sk[C::STEPS];                // dS^T (bf16)
   constexpr int NX = 2 * C::KST * C::NSUB;  // MFMAs of X
   constexpr int NZ = C::STEPS * C::DSUB;    // MFMAs of Z
-  auto X = [&](int bf) __attribute__((always_inline)) {
-    const uint8_t* kt = ks[bf];
-    const uint8_t* vt = vs[bf];
+  auto X = [&](const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < C::NSUB; ++n) {
       sA[n] = f32x16{};
@@ -584,7 +585,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     schedule_mfma_reads<NX - 4, 1, 4>();
   };
-  auto Y = [&](int j, int jd, int bfd) __attribute__((always_inline)) {
+  // vector phase of block j; the loading group issues its DMA slots between
+  // the exponentials (a burst would stall the wave for the whole transfer)
+  auto Y = [&](int j, auto&& issue) __attribute__((always_inline)) {
     const int kv0 = j * BK;
     if ((CAUSAL && kv0 + BK - 1 > wq0) || (kv0 + BK > N_kv)) {
       const int last_key = CAUSAL ? min(query, N_kv - 1) : N_kv - 1;
@@ -602,7 +605,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float pv = fast_exp2(fmaf(sA[n][i], c, -l2));
         pA[n][i] = pv * (pA[n][i] - dl);
         const int e = 16 * n + i;
-        if (e % 3 == 1 && e / 3 < kSlots) dma_slot(e / 3, jd, bfd);
+        if (e % 3 == 1 && e / 3 < kSlots) issue(e / 3);
       }
 #pragma unroll
       for (int w = 0; w < 2; ++w)
@@ -610,10 +613,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int e = 0; e < 4; ++e) sk[2 * n + w][e] = cvt_pk_bf16(pA[n][8 * w + 2 * e], pA[n][8 * w + 2 * e + 1]);
     }
 #pragma unroll
-    for (int e = 32 * C::NSUB / 3 + 1; e < kSlots; ++e) dma_slot(e, jd, bfd);
+    for (int e = 32 * C::NSUB / 3 + 1; e < kSlots; ++e) issue(e);
+    // dS is packed in this phase: left alone, the compiler sinks the packing
+    // past the barrier into the MFMAs of the next one
+#pragma unroll
+    for (int u = 0; u < C::STEPS; ++u) asm volatile("" : "+v"(sk[u]));
   };
-  auto Z = [&](int bf) __attribute__((always_inline)) {
-    const uint8_t* kt = ks[bf];
+  auto Z = [&](const uint8_t* kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < C::STEPS; ++u) {
       const int rb = (32 * (u >> 1) + 8 * (u & 1)) * C::ROW_BYTES;
@@ -625,24 +631,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     schedule_mfma_reads<NZ - 4, 2, 8>();
   };
+  // MFMA phase of block j: Z(j-1) then X(j); block j lives in ring buffer BF
+  // (a compile-time constant, so that LDS addresses are offsets plus
+  // immediates)
+  auto mfma_phase = [&](int j, auto bfc) __attribute__((always_inline)) {
+    constexpr int BF = decltype(bfc)::value;
+    constexpr int BFP = (BF + kDqRing - 1) % kDqRing;
+    if (j >= 1) Z(ks[BFP]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < nblk) X(ks[BF], vs[BF]);
+  };
+  auto no_dma = [](int) __attribute__((always_inline)) {};
 
-  // block 0 into buffer 0; block j+1 is loaded into the other buffer while
-  // block j is processed (the buffer's previous block was finished before
-  // the last barrier)
+  // prologue: block 0 into buffer 0
+  if (grp == 1) {
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < nblk; ++j) {
-    const int bf = j & 1;
-    const int jd = min(j + 1, nblk - 1);  // past the end: a harmless reload
-    X(bf);
-    __builtin_amdgcn_sched_barrier(0);
-    Y(j, jd, bf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    Z(bf);
+    for (int i = 0; i < kSlots; ++i) dma_slot(i, 0, ks[0], vs[0]);
     wait_vmem();
-    barrier_nofence();
+  }
+  __syncthreads();
+
+  if (grp == 0) {
+    auto a_block = [&](int j, auto bfc) __attribute__((always_inline)) {
+      mfma_phase(j, bfc);
+      barrier_nofence();
+      if (j < nblk) Y(j, no_dma);
+      barrier_nofence();
+    };
+    for (int j = 0; j <= nblk; j += kDqRing) {
+      a_block(j, std::integral_constant<int, 0>{});
+      if (j + 1 <= nblk) a_block(j + 1, std::integral_constant<int, 1>{});
+      if (j + 2 <= nblk) a_block(j + 2, std::integral_constant<int, 2>{});
+    }
+  } else {
+    // block 0: the load of block 1, then X(0)
+    {
+      const int jn = min(1, nblk - 1);
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i) dma_slot(i, jn, ks[1], vs[1]);
+      barrier_nofence();
+      mfma_phase(0, std::integral_constant<int, 0>{});
+      wait_vmem();
+      barrier_nofence();
+    }
+    auto b_block = [&](int j, auto bfc) __attribute__((always_inline)) {
+      constexpr int BF = decltype(bfc)::value;
+      constexpr int BFN = (BF + 1) % kDqRing;  // block j+1 (the buffer of block j-2)
+      const int jn = min(j + 1, nblk - 1);     // past the end: a harmless reload into a free buffer
+      Y(j - 1, [&](int i) __attribute__((always_inline)) { dma_slot(i, jn, ks[BFN], vs[BFN]); });
+      barrier_nofence();  // the DMA stays in flight through the next phase
+      mfma_phase(j, bfc);
+      wait_vmem();        // block j+1 is in LDS before the barrier publishes it
+      barrier_nofence();
+    };
+    for (int j = 1; j <= nblk; j += kDqRing) {
+      b_block(j, std::integral_constant<int, 1>{});
+      if (j + 1 <= nblk) b_block(j + 1, std::integral_constant<int, 2>{});
+      if (j + 2 <= nblk) b_block(j + 2, std::integral_constant<int, 0>{});
+    }
   }
 
   if (query < N_q) {
@@ -675,8 +721,8 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
                      dim3(kPairThreads), 0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dk, p.dv,
                      p.H_q, p.H_kv, p.N_q, p.N_kv, n_ktiles, xcd_remap, c, p.scale);
-  const int n_qtiles = (p.N_q + kQueriesPerWg - 1) / kQueriesPerWg;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_qtiles * p.B * p.H_q)), dim3(kThreads),
+  const int n_qtiles = (p.N_q + kDqRows - 1) / kDqRows;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_qtiles * p.B * p.H_q)), dim3(kDqThreads),
                      0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dq, p.H_q,
                      p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, p.B * p.H_q, c, p.scale);
