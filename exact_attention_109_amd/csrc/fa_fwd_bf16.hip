@@ -12,13 +12,16 @@
 // --------------
 //  * Workgroup = 8 wave64s, 256 query rows (32 per wave), one workgroup per
 //    CU (2 waves per SIMD). All tiles of one key/value head go to one XCD.
-//    Causal dense calls: a workgroup takes two tiles of one head, r and
-//    n-1-r, one after the other, so that every workgroup costs the same (the
-//    dispatcher starts an XCD's workgroups a few at a time and in order, so
-//    unequal neighbours leave compute units idle) while one head's tiles stay
-//    neighbours in the grid (their K/V is shared through L2). Otherwise one
-//    workgroup per (batch, query head, 256-row tile), causal tiles heaviest
-//    first and dealt rank by rank over groups of four heads.
+//    Causal dense calls at d = 128: a workgroup takes two tiles of one head,
+//    r and n-1-r, one after the other, so that every workgroup costs the same
+//    (the dispatcher starts an XCD's workgroups a few at a time and in order,
+//    so unequal neighbours leave compute units idle) while one head's tiles
+//    stay neighbours in the grid (their K/V is shared through L2). Otherwise
+//    one workgroup per (batch, query head, 256-row tile), causal tiles
+//    heaviest first and dealt rank by rank over groups of four heads. (At
+//    d = 64 the loop over two tiles would keep values from outside the block
+//    loop alive through it and push the kernel past 256 registers into
+//    spills inside the loop.)
 //  * Contractions on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The
 //    scores are computed transposed, S^T = K Q^T (K as the A operand, Q as B),
 //    so that a lane owns one query column; P^T then feeds O^T = V^T P^T as the
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int hk = kvidx % H_kv;
   const int h = hk * G + gq;
   const int tile_hi = CAUSAL ? (n_qtiles - 1 - tile_rank) : tile_rank;  // heaviest first
-  const int n_it = (paired && tile_rank != tile_hi) ? 2 : 1;
+  const int n_it = (D == 128 && paired && tile_rank != tile_hi) ? 2 : 1;  // (launch sets paired only at d = 128)
 
   // Dense: q, o [B][H_q][N_q][D], k, v [B][H_kv][N_kv][D], lse [B][H_q][N_q].
   // Packed sequences (cu_q != null): b is a sequence, q, o [H_q][total_q][D],
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream) {
   const int n_qtiles = (p.N_q + kBR - 1) / kBR;
-  const int paired = (CAUSAL && vl == nullptr) ? 1 : 0;
+  const int paired = (D == 128 && CAUSAL && vl == nullptr) ? 1 : 0;
   const long long nwg = (long long)(paired ? (n_qtiles + 1) / 2 : n_qtiles) * p.B * p.H_q;
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
   // Masked scores are -inf and exp2(-inf * c) must be 0, so c stays positive:
