@@ -56,6 +56,9 @@
 //    saves the max of every other block.
 //  * Causal: K/V blocks past the tile's last row are never loaded; masking
 //    runs only on blocks that cross a wave's diagonal or the end of the keys.
+//  * d = 64 runs fwd_bf16_rot_kernel (below): four waves per SIMD in a
+//    four-group rotation, for the vector work that outweighs the matrix work
+//    about twice at that head size.
 
 #include <type_traits>
 
@@ -79,7 +82,7 @@ constexpr int kSgDsRead = 0x100;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BC = 8192 / D;              // keys per block: 64 (d=128), 128 (d=64)
+  static constexpr int BC = 8192 / D;              // keys per block: 64 at d=128 (d=64 calls run the rotation kernel)
   static constexpr int NSUB = BC / 32;             // 32-key subtiles of S^T
   static constexpr int DSUB = D / 32;              // 32-column subtiles of O^T
   static constexpr int QK_STEPS = D / 16;          // MFMA k-steps over the head dimension
@@ -562,16 +565,374 @@ hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// d = 64: four-group rotation.
+//
+// At d = 64 a key block costs the vector ALU about twice what it costs the
+// matrix cores (the softmax work per score is the same as at d = 128, the
+// MFMA work half). With two waves per SIMD in ping-pong, one softmax wave
+// runs beside one MFMA wave and the matrix cores idle half the time. A
+// single wave also issues vector instructions well below the SIMD's rate;
+// two or three softmax waves on one SIMD together get 1.35-1.6x the
+// throughput of one, while an MFMA wave beside them keeps its rate.
+//
+// So this kernel runs 16 waves (four per SIMD) in four groups of four, 512
+// query rows per workgroup. Time is cut into ticks, one workgroup barrier
+// each. Group g runs the MFMA phase of key block j (PV of block j-1, QK^T of
+// block j) in tick 4j + g, and the softmax of block j in the three ticks
+// after it, a third of the scores per tick. So in every tick one wave of each
+// SIMD drives the matrix core and three share the vector ALU (the scores
+// are split 12 / 8 / 12 over the three ticks; the middle one also issues the
+// DMA, which stalls the issuing wave until the load path takes it).
+//
+// K and V blocks (64 keys) stream through three-buffer LDS rings. In the
+// second softmax tick of block j (tick 4j+g+2), every wave issues one 1 KiB
+// LDS-DMA piece: groups 0-1 of K_{j+2}, groups 2-3 of V_{j+1}. K_b is read
+// in ticks 4b .. 4b+3 and V_b (for PV of block b) in ticks 4b+4 .. 4b+7, so
+// each target buffer was last read at tick 4j-1, before the first issue at
+// 4j+2. Each wave waits for its piece at the end of its next MFMA phase
+// (tick 4j+4+g), whose barrier publishes it before its first reader (tick
+// 4j+8).
+// ---------------------------------------------------------------------------
+constexpr int kRotGroups = 4;
+constexpr int kRotWaves = 4 * kRotGroups;
+constexpr int kRotThreads = 64 * kRotWaves;
+constexpr int kRotBR = 32 * kRotWaves;  // query rows per workgroup
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kRotThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_bf16_rot_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int H_q, int H_kv, int N_q_arg, int N_kv_arg, int n_qtiles, int xcd_remap, float c,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
+  constexpr int D = 64;
+  constexpr int BC = 64;                 // keys per block
+  constexpr int NSUB = BC / 32;          // 32-key subtiles of S^T
+  constexpr int DSUB = D / 32;           // 32-column subtiles of O^T
+  constexpr int QK_STEPS = D / 16;
+  constexpr int PV_STEPS = BC / 16;
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;          // rows per 1 KiB DMA piece
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int TILE_BYTES = BC * ROW_BYTES;    // 8 KiB: 8 pieces
+  constexpr int PIECES = TILE_BYTES / 1024;
+  static_assert(2 * PIECES == kRotWaves, "one DMA piece per wave and block");
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb2[TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;    // rotation group
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int G = H_q / H_kv;
+
+  const TileAssign ta = assign_tile(blockIdx.x, n_qtiles, G, xcd_remap, (int)(gridDim.x / n_qtiles), false,
+                                    CAUSAL ? 4 : 1);
+  const int kvidx = ta.kvidx, gq = ta.gq;
+  const int b = kvidx / H_kv;
+  const int hk = kvidx % H_kv;
+  const int h = hk * G + gq;
+  const int tile = CAUSAL ? (n_qtiles - 1 - ta.tile_rank) : ta.tile_rank;  // heaviest first
+
+  // layouts as in fwd_bf16_kernel (dense, or packed sequences with clamped offsets)
+  int N_q = N_q_arg, N_kv = N_kv_arg;
+  size_t qbase, kvbase, lbase;
+  if (cu_q != nullptr) {
+    const int qs = min(max(cu_q[b], 0), total_q);
+    const int qe = min(max(cu_q[b + 1], qs), total_q);
+    const int ks = min(max(cu_k[b], 0), total_k);
+    const int ke = min(max(cu_k[b + 1], ks), total_k);
+    N_q = min(qe - qs, N_q_arg);
+    N_kv = ke - ks;
+    qbase = (size_t(h) * total_q + qs) * D;
+    kvbase = (size_t(hk) * total_k + ks) * D;
+    lbase = size_t(h) * total_q + qs;
+  } else {
+    qbase = (size_t(b) * H_q + h) * size_t(N_q) * D;
+    kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
+    lbase = (size_t(b) * H_q + h) * size_t(N_q);
+  }
+  const int q0 = tile * kRotBR;
+  if (q0 >= N_q) return;  // (whole workgroup) a tile past a short sequence
+  if (N_kv == 0) {
+    const int row = q0 + wave * 32 + col;
+    if (row < N_q) {
+      uint16_t* op = O + qbase + size_t(row) * D + half * (D / 2);
+#pragma unroll
+      for (int j = 0; j < D / 2; j += 4) st_global8(op + j, u32x2{0u, 0u});
+      if (half == 0) LSE[lbase + row] = -INFINITY;
+    }
+    return;
+  }
+  const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
+  const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
+
+  const int wrow0 = q0 + wave * 32;
+  const int qrow = wrow0 + col;
+  bf16x8 qreg[QK_STEPS];
+  {
+    const uint16_t* qp = Q + qbase + size_t(min(qrow, N_q - 1)) * D + half * (D / 2);
+#pragma unroll
+    for (int t = 0; t < QK_STEPS; ++t) qreg[t] = as_bf16x8(ld_global16(qp + 8 * t));
+  }
+  const int nblk_all = (N_kv + BC - 1) / BC;
+  int nblk = nblk_all;
+  if (CAUSAL) nblk = min(nblk_all, (min(q0 + kRotBR, N_q) - 1) / BC + 1);
+  auto need_mask = [&](int j) __attribute__((always_inline)) {
+    const int kv0 = j * BC;
+    return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
+  };
+
+  // ---- LDS-DMA pieces. Piece p (0..7) of a tile covers rows RPI*p ..
+  // RPI*p + RPI-1; lane l writes 16 bytes of row RPI*p + l/CPR (physical
+  // chunk l%CPR, holding logical chunk (l%CPR) ^ swz(row)). The tail block
+  // reads clamped rows (finite data for masked keys, nothing past the end).
+  const int tail_blk = (N_kv % BC) ? N_kv / BC : -1;
+  const int tail_lim = N_kv - 1 - (N_kv / BC) * BC;
+  auto piece_off = [&](int p, bool is_k, int jb) __attribute__((always_inline)) {
+    const int row = RPI * p + lane / CPR;
+    const int ch = lane % CPR;
+    const int r = (jb == tail_blk) ? min(row, tail_lim) : row;
+    return uint32_t(r * ROW_BYTES + ((ch ^ (is_k ? swz_k<D>(row) : swz_v<D>(row))) * 16));
+  };
+  auto dma_piece = [&](int p, bool is_k, int jb, uint8_t* dst) __attribute__((always_inline)) {
+    const uint8_t* src = (is_k ? Kbytes : Vbytes) + size_t(jb) * BC * ROW_BYTES;
+    lds_dma16_sbase(src, piece_off(p, is_k, jb), lds_address(dst) + 1024 * p);
+  };
+  // this wave's piece in the loop: groups 0-1 stage K, groups 2-3 stage V
+  const int my_piece = wave & (PIECES - 1);
+  const bool my_k = wave < PIECES;
+
+  // ---- LDS read offsets (as fwd_bf16_kernel at d = 64)
+  const int krow = row_of_lane(col);
+  int koff[QK_STEPS];
+#pragma unroll
+  for (int t = 0; t < QK_STEPS; ++t) koff[t] = krow * ROW_BYTES + ((((D / 16) * half + t) ^ swz_k<D>(krow)) * 16);
+  const int j16 = lane & 15;
+  const int vgrp = (lane & 31) >> 4;
+  int voff[DSUB];
+#pragma unroll
+  for (int s = 0; s < DSUB; ++s) {
+    const int row = 16 * half + (j16 >> 2);
+    const int cc = 32 * s + 16 * vgrp + 4 * (j16 & 3);
+    voff[s] = row * ROW_BYTES + (((cc >> 3) ^ swz_v<D>(row)) * 16) + (cc & 7) * 2;
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  float psum = 0.f;
+  bool eager = true;
+  bool moved = false;
+  f32x16 oacc[DSUB];
+#pragma unroll
+  for (int s = 0; s < DSUB; ++s) oacc[s] = f32x16{};
+  f32x16 sacc[NSUB];
+  u32x4 pk[PV_STEPS];
+
+  auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    if (j >= 1) {
+#pragma unroll
+      for (int u = 0; u < PV_STEPS; ++u) {
+        const int rbase = (32 * (u >> 1) + 8 * (u & 1)) * ROW_BYTES;
+#pragma unroll
+        for (int s = 0; s < DSUB; ++s)
+          oacc[s] = mfma32x32x16(lds_read_tr8(vt + voff[s] + rbase, vt + voff[s] + rbase + 4 * ROW_BYTES),
+                                 as_bf16x8(pk[u]), oacc[s]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+#pragma unroll
+      for (int i = 0; i < PV_STEPS * DSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      }
+    }
+    if (j < nblk) {
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n) sacc[n] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < QK_STEPS; ++t)
+#pragma unroll
+        for (int n = 0; n < NSUB; ++n)
+          sacc[n] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[t] + n * 32 * ROW_BYTES)),
+                                 qreg[t], sacc[n]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+#pragma unroll
+      for (int i = 0; i < QK_STEPS * NSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      }
+    }
+  };
+
+  // Softmax of a block in three parts. Quad q (0..7) = scores
+  // sacc[q/4][4(q%4) .. 4(q%4)+3], packed into pk[q/2][2(q%2)], [2(q%2)+1].
+  auto exp_quad = [&](int q) __attribute__((always_inline)) {
+    const int n = q >> 2, w4 = (q & 3) * 4;
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = fast_exp2(fmaf(sacc[n][w4 + e], c, -m_run));
+      psum += p[e];
+    }
+    pk[q >> 1][2 * (q & 1)] = cvt_pk_bf16(p[0], p[1]);
+    pk[q >> 1][2 * (q & 1) + 1] = cvt_pk_bf16(p[2], p[3]);
+  };
+  auto block_max = [&]() __attribute__((always_inline)) {
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
+    return max_xor32(mx) * c;
+  };
+  auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int s = 0; s < DSUB; ++s)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
+    m_run = m_new;
+  };
+  auto soft1 = [&](int j) __attribute__((always_inline)) {
+    if (j >= nblk) return;
+    if (need_mask(j)) {
+      const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
+      const int lim = last_key - j * BC - 16 * half;
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * n + i > lim) sacc[n][i] = -INFINITY;
+    }
+    moved = false;
+    if (eager) {
+      const float m_blk = block_max();
+      if (__any(m_blk > m_run + kRescaleSlack)) {
+        rescale_to(fmaxf(m_run, m_blk));
+        moved = true;
+      }
+    }
+    psum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) exp_quad(q);
+  };
+  auto soft2 = [&](int j, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+    if (j >= nblk) return;
+    // the DMA pieces of K_{j+2} / V_{j+1} (past the end, a block again into a free buffer)
+    if (my_k) dma_piece(my_piece, true, min(j + 2, nblk - 1), kd);
+    else dma_piece(my_piece, false, min(j + 1, nblk - 1), vd);
+#pragma unroll
+    for (int q = 3; q < 5; ++q) exp_quad(q);
+  };
+  auto soft3 = [&](int j) __attribute__((always_inline)) {
+    if (j >= nblk) return;
+#pragma unroll
+    for (int q = 5; q < 8; ++q) exp_quad(q);
+    // a row's block sum above 2^8 (or inf / NaN): form the block max, rescale
+    // and take the block's exponentials again
+    if (__any(!(psum <= 256.0f))) {
+      const float m_new = fmaxf(m_run, block_max());
+      if (__any(m_new > m_run)) {
+        rescale_to(m_new);
+        psum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) exp_quad(q);
+        moved = true;
+      }
+    }
+    eager = moved;
+    l_run += psum;
+    // keep the row sum and the packed operands in this tick
+    asm volatile("" : "+v"(l_run));
+#pragma unroll
+    for (int u = 0; u < PV_STEPS; ++u) asm volatile("" : "+v"(pk[u]));
+  };
+
+  // ---- prologue: K_0, K_1 and V_0 (24 pieces over 16 waves)
+  dma_piece(wave & 7, true, wave < 8 ? 0 : min(1, nblk - 1), wave < 8 ? kb0 : kb1);
+  if (wave < 8) dma_piece(wave, false, 0, vb0);
+  wait_vmem();
+  __syncthreads();
+
+  // ---- the rotation: group g waits g ticks, runs 4 ticks per block for
+  // blocks 0..nblk (the extra block only finishes PV), then waits 3-g ticks;
+  // every wave passes 4 (nblk + 1) + 3 barriers. Blocks are taken three at a
+  // time so that every ring buffer is a compile-time choice:
+  // K_j in kb[j%3], V_{j-1} in vb[(j-1)%3], DMA into kb[(j+2)%3], vb[(j+1)%3].
+  for (int i = 0; i < grp; ++i) barrier_nofence();
+  auto step = [&](int j, const uint8_t* kc, const uint8_t* vp, uint8_t* kd, uint8_t* vd)
+      __attribute__((always_inline)) {
+    mfma_phase(j, kc, vp);
+    wait_vmem();  // this wave's DMA piece from the previous block
+    barrier_nofence();
+    soft1(j);
+    barrier_nofence();
+    soft2(j, kd, vd);
+    barrier_nofence();
+    soft3(j);
+    barrier_nofence();
+  };
+  for (int j = 0; j <= nblk; j += 3) {
+    step(j, kb0, vb2, kb2, vb1);
+    if (j + 1 <= nblk) step(j + 1, kb1, vb0, kb0, vb2);
+    if (j + 2 <= nblk) step(j + 2, kb2, vb1, kb1, vb0);
+  }
+  for (int i = grp; i < kRotGroups - 1; ++i) barrier_nofence();
+
+  // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+  const float l_tot = sum_xor32(l_run);
+  if (qrow < N_q) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* op = O + qbase + size_t(qrow) * D;
+#pragma unroll
+    for (int s = 0; s < DSUB; ++s) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w;
+        w[0] = cvt_pk_bf16(oacc[s][4 * a + 0] * inv, oacc[s][4 * a + 1] * inv);
+        w[1] = cvt_pk_bf16(oacc[s][4 * a + 2] * inv, oacc[s][4 * a + 3] * inv);
+        st_global8(op + 32 * s + 8 * a + 4 * half, w);
+      }
+    }
+    if (half == 0) LSE[lbase + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_rot(const FwdParams& p, const VarlenParams* vl, hipStream_t stream) {
+  const int n_qtiles = (p.N_q + kRotBR - 1) / kRotBR;
+  const long long nwg = (long long)n_qtiles * p.B * p.H_q;
+  const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
+  const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
+  hipLaunchKernelGGL((fwd_bf16_rot_kernel<CAUSAL>), dim3((unsigned)nwg), dim3(kRotThreads), 0, stream,
+                     static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                     static_cast<const uint16_t*>(p.v), static_cast<uint16_t*>(p.o), p.lse,
+                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_qtiles, xcd_remap, c,
+                     vl ? vl->cu_q : nullptr, vl ? vl->cu_k : nullptr, vl ? vl->total_q : 0,
+                     vl ? vl->total_k : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (p.d == 128) return p.causal ? launch<128, true>(p, nullptr, stream) : launch<128, false>(p, nullptr, stream);
-  return p.causal ? launch<64, true>(p, nullptr, stream) : launch<64, false>(p, nullptr, stream);
+  return p.causal ? launch_rot<true>(p, nullptr, stream) : launch_rot<false>(p, nullptr, stream);
 }
 
 hipError_t launch_fwd_varlen_bf16(const FwdParams& p, const VarlenParams& vl, hipStream_t stream) {
   if (p.d == 128) return p.causal ? launch<128, true>(p, &vl, stream) : launch<128, false>(p, &vl, stream);
-  return p.causal ? launch<64, true>(p, &vl, stream) : launch<64, false>(p, &vl, stream);
+  return p.causal ? launch_rot<true>(p, &vl, stream) : launch_rot<false>(p, &vl, stream);
 }
 
 }  // namespace fa
