@@ -39,6 +39,8 @@ CASES = [
     ([17, 3, 256, 511], [40, 3, 256, 1000], 8, 2, 128, False),  # N_q != N_kv
     ([100, 33, 260], [100, 33, 260], 4, 4, 64, True),
     ([3, 10], [0, 10], 2, 1, 128, False),                        # a sequence without keys
+    ([3, 10, 6], [0, 10, 70], 2, 1, 64, True),                   # the same at d = 64, causal
+    ([600, 5], [600, 700], 2, 2, 64, True),                      # d = 64, two 512-row query tiles
 ]
 
 
@@ -63,10 +65,11 @@ def test_each_sequence_against_oracle(case):
         assert max_abs(lse[None, :, qs:qe], L) <= TOL[DTYPE_BF16]["lse"], s
 
 
-def test_equal_lengths_match_the_dense_path_bitwise():
+@pytest.mark.parametrize("d", [64, 128])
+def test_equal_lengths_match_the_dense_path_bitwise(d):
     import exact_attention_109_amd as fa
     import torch
-    B, Hq, Hkv, n, d = 3, 8, 2, 300, 128
+    B, Hq, Hkv, n = 3, 8, 2, 300
     inp = make_inputs_shape(DTYPE_BF16, B, Hq, Hkv, n, n, d, seed=951)
     q, k, v = (inp.torch(x, "cuda") for x in ("q", "k", "v"))
     for causal in (False, True):
