@@ -211,7 +211,10 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int t = 0; t < C::KST; ++t) kv[t] = as_bf16x8(ld_global16(src + off + 8 * t));
   }
-  wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
+  // (no wait here: these loads stay in flight with the prologue's LDS-DMA.
+  // Vector-memory operations retire in order, so the compiler's own waits
+  // for kv, which do not count the DMA, are only ever stricter than needed,
+  // and the prologue's barrier waits for everything.)
 
   const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
   const int nqb = qstart < N_q ? (N_q - qstart + BQ - 1) / BQ : 0;
@@ -528,7 +531,8 @@ __global__ __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   const float l2 = L2[rbase + qc];
   const float dl = Dl[rbase + qc];
-  wait_vmem();  // the LDS-DMA below is not tracked by the compiler's waits
+  // (no wait here: these loads stay in flight with the prologue's LDS-DMA;
+  // see bwd_dkdv_pair_kernel)
 
   // key blocks of the workgroup; every wave runs all of them (blocks past a
   // wave's queries are masked to zero)
