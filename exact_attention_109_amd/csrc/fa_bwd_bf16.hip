@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dl,
     float* __restrict__ dK, float* __restrict__ dV, int H_q, int H_kv, int N_q, int N_kv, int n_ktiles,
-    int xcd_remap, float c, float scale) {
+    int xcd_remap, float c, float scale, int paired) {
   using C = BwdCfg<D>;
   constexpr int BQ = C::BLK;
   constexpr int DPW = C::DMA_PER_WAVE;   // 1 KiB pieces of a tile per loading (dS) wave
@@ -194,10 +194,22 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int half = lane >> 5;
   const int G = H_q / H_kv;
 
-  const TileAssign ta = assign_tile(blockIdx.x, n_ktiles, 1, xcd_remap);
+  // Causal: a workgroup takes key tiles r and n-1-r of one head (tile r has
+  // the most query blocks to visit), so that every workgroup costs the same.
+  const int n_units = paired ? (n_ktiles + 1) / 2 : n_ktiles;
+  const TileAssign ta = assign_tile(blockIdx.x, n_units, 1, xcd_remap);
   const int b = ta.kvidx / H_kv;
   const int hk = ta.kvidx % H_kv;
-  const int k0 = ta.tile_rank * kKeysPerWg;
+  const int rank2 = n_ktiles - 1 - ta.tile_rank;
+  // The tile body is inlined twice rather than looped: a loop around it kept
+  // values of the first tile alive through the second and spilled registers.
+  auto do_tile = [&](const int tile_rank) __attribute__((always_inline)) {
+  int lane_t = tid & 63;
+  asm volatile("" : "+v"(lane_t));  // per-lane values are recomputed per tile, not kept across both
+  const int lane = lane_t;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int k0 = tile_rank * kKeysPerWg;
   const int kw = k0 + 32 * pw;     // first key of this pair
   const int key = kw + col;        // this lane's key (MFMA column)
   const size_t kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
@@ -466,6 +478,12 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
     }
   }
   (void)n_slots;
+  };
+  do_tile(ta.tile_rank);
+  if (paired && rank2 != ta.tile_rank) {
+    barrier_nofence();  // every wave is done with the first tile's LDS
+    do_tile(rank2);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -721,10 +739,12 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const float c = fmaxf(p.scale * kLog2e, 1.17549435e-38f);
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
   const int n_ktiles = (p.N_kv + kKeysPerWg - 1) / kKeysPerWg;
-  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_ktiles * p.B * p.H_kv)),
+  const int paired = CAUSAL ? 1 : 0;
+  const int n_units = paired ? (n_ktiles + 1) / 2 : n_ktiles;
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_units * p.B * p.H_kv)),
                      dim3(kPairThreads), 0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
                      static_cast<const uint16_t*>(p.v), static_cast<const uint16_t*>(p.dO), L2, Dl, p.dk, p.dv,
-                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_ktiles, xcd_remap, c, p.scale);
+                     p.H_q, p.H_kv, p.N_q, p.N_kv, n_ktiles, xcd_remap, c, p.scale, paired);
   const int n_qtiles = (p.N_q + kDqRows - 1) / kDqRows;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)n_qtiles * p.B * p.H_q)), dim3(kDqThreads),
                      0, stream, static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
