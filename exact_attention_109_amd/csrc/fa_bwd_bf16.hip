@@ -148,10 +148,12 @@ constexpr int kKeysPerWg = 128;  // keys per dK/dV workgroup: 4 wave pairs x 32 
 // and w + 4 (w = 0..3) run on the same SIMD and own the same 32 keys:
 //   P wave  (w):     S = Q K^T, P = exp2(S c - L2) (masked), dV^T += dO^T P
 //   dS wave (w + 4): dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
-// P goes from the P wave to its dS wave through LDS in float32, lane for lane
-// (both waves compute their scores in the same accumulator layout, so lane l
-// register i of one is lane l register i of the other). Two ticks per query
-// block j, each ended by a workgroup barrier:
+// P goes from the P wave to its dS wave through LDS lane for lane (both waves
+// compute their scores in the same accumulator layout, so lane l register i of
+// one is lane l register i of the other), as the bf16 pairs the dV product
+// takes: half the LDS bytes of float32, and dS = P (dP - D) is rounded to bf16
+// for its own product anyway, so the extra rounding of P is of the same order.
+// Two ticks per query block j, each ended by a workgroup barrier:
 //   tick 1: P wave:  S(j), then P(j) and its hand-over (vector work);
 //           dS wave: dK += Q(j-1)^T dS(j-1), then dP(j)          (MFMA)
 //   tick 2: P wave:  dV += dO(j)^T P(j)                            (MFMA);
@@ -179,11 +181,10 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
   using C = BwdCfg<D>;
   constexpr int BQ = C::BLK;
   constexpr int DPW = C::DMA_PER_WAVE;   // 1 KiB pieces of a tile per loading (dS) wave
-  constexpr int NG = C::NSUB * 4;        // groups of 4 score registers per lane
   __shared__ __attribute__((aligned(1024))) uint8_t qs[kPairRing][C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t os[kPairRing][C::TILE_BYTES];
   __shared__ __attribute__((aligned(256))) float vecs[kPairRing][2][BQ];  // [buffer][L2, D][query]
-  __shared__ __attribute__((aligned(1024))) f32x4 pex[4][NG][64];         // [pair][register group][lane]
+  __shared__ __attribute__((aligned(1024))) u32x4 pex[4][C::STEPS][64];   // [pair][packed P register][lane], bf16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,12 +366,13 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
             pv[e] = fast_exp2(fmaf(sx[n][4 * v4 + e], c, -a[e]));
             sx[n][4 * v4 + e] = pv[e];
           }
-          pex[pw][4 * n + v4][lane] = pv;
         }
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
+        for (int w = 0; w < 2; ++w) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) pk[2 * n + w][e] = cvt_pk_bf16(sx[n][8 * w + 2 * e], sx[n][8 * w + 2 * e + 1]);
+          pex[pw][2 * n + w][lane] = pk[2 * n + w];  // the hand-over: P in bf16, as the dV product uses it
+        }
       }
       // P(j) is packed in this tick: left alone, the compiler sinks the
       // packing past the barrier into the dV MFMAs of the next one
@@ -421,12 +423,17 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
       const float* dt = vecs[BF][1];
 #pragma unroll
       for (int n = 0; n < C::NSUB; ++n) {
+        const u32x4 pb[2] = {pex[pw][2 * n][lane], pex[pw][2 * n + 1][lane]};
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + 32 * n + 16 * half + 4 * v4);
-          const f32x4 pv = pex[pw][4 * n + v4][lane];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) px[n][4 * v4 + e] = pv[e] * (px[n][4 * v4 + e] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            // score 4 v4 + e of the subtile: packed register v4/2, pair 2 (v4%2) + e/2, half e%2
+            const uint32_t w2 = pb[v4 >> 1][2 * (v4 & 1) + (e >> 1)];
+            const float pv = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+            px[n][4 * v4 + e] = pv * (px[n][4 * v4 + e] - d4[e]);
+          }
           const int slot = 4 * n + v4;
           if (slot < 2 * DPW) dma_slot(slot, jd, BFP);
         }
