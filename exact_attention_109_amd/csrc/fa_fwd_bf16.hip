@@ -16,7 +16,10 @@
 //    r and n-1-r, one after the other, so that every workgroup costs the same
 //    (the dispatcher starts an XCD's workgroups a few at a time and in order,
 //    so unequal neighbours leave compute units idle) while one head's tiles
-//    stay neighbours in the grid (their K/V is shared through L2). Otherwise
+//    stay neighbours in the grid (their K/V is shared through L2). The
+//    lighter tile runs second and visits its key blocks from the diagonal
+//    down, so that all workgroups of a head read the same K/V block at each
+//    step of both tiles. Otherwise
 //    one workgroup per (batch, query head, 256-row tile), causal tiles
 //    heaviest first and dealt rank by rank over groups of four heads. (At
 //    d = 64 the loop over two tiles would keep values from outside the block
@@ -219,8 +222,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int last_row = min(q0 + kBR, N_q) - 1;
       nblk = min(nblk_all, last_row / BC + 1);
     }
-    auto need_mask = [&](int j) __attribute__((always_inline)) {
-      const int kv0 = j * BC;
+    // Order of the key blocks. Causal, the lighter tile of a mirror pair (t
+    // and n-1-t, n the sequence's tile count) takes its diagonal blocks first
+    // and then the others from the diagonal down to block 0; every other tile
+    // goes from block 0 up. A workgroup runs its heavier tile first, so the
+    // workgroups of a head, running side by side, all read key block b at the
+    // same step: step b while ascending, step 4n+3-b while descending. Each
+    // block is fetched from HBM once for all of them. Had the lighter tile
+    // restarted at block 0, the workgroups would reach each block at staggered
+    // steps and L2 would have evicted it in between. The first block visited
+    // shows every row at least one key (its own diagonal block or, with no
+    // diagonal block, one wholly below the tile).
+    const int n_own = (N_q + kBR - 1) / kBR;
+    const int dlo = (CAUSAL && tile < n_own - 1 - tile) ? min(q0 / BC, nblk) : 0;
+    const int n_asc = nblk - dlo;
+    auto blk = [&](int j) __attribute__((always_inline)) { return j < n_asc ? dlo + j : nblk - 1 - j; };
+    auto need_mask = [&](int jb) __attribute__((always_inline)) {
+      const int kv0 = jb * BC;
       return (CAUSAL && kv0 + BC - 1 > wrow0) || (kv0 + BC > N_kv);
     };
 
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // K_0 for the prologue (only group B calls it)
     auto dma_k0 = [&](uint8_t* kdst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_slot(i, 0, 0, kdst, kdst);
+      for (int i = 0; i < C::DMA_PER_WAVE; ++i) dma_slot(i, blk(0), blk(0), kdst, kdst);
     };
 
     // ---- per-lane LDS read offsets (bytes within a tile)
@@ -377,12 +395,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if constexpr (!kDma) {
         if (j >= nblk) return;  // the step that only finishes PV of the last block
       }
-      if (need_mask(j)) {
+      const int jb = blk(j);
+      if (need_mask(jb)) {
         // key kv0 + 32n + 16*half + i is visible iff it is <= last_key (the
         // row itself when causal, and < N_kv); one compare against the
         // register's constant key offset per score.
         const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
-        const int lim = last_key - j * BC - 16 * half;
+        const int lim = last_key - jb * BC - 16 * half;
 #pragma unroll
         for (int n = 0; n < NSUB; ++n)
 #pragma unroll
@@ -469,7 +488,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // consumed by an MFMA of the same phase, so a buffer is free for the next
     // DMA once the barrier after its last reading phase has passed, and DMA
     // data is waited for explicitly one phase after it was issued.
-    // Buffers: K_j in kb[j%2], V_j in vb[j%2]. Each group runs its own loop
+    // Buffers: step j's K and V blocks in kb[j%2], vb[j%2]. Each group runs its own loop
     // (the group test is outside the loop, so the compiler never has to keep
     // both groups' register state alive across the barriers); both loops pass
     // the same 2*(nblk+1) barriers.
@@ -483,8 +502,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __attribute__((always_inline)) {
       // K_{j+1} and V_j; past the last block the last one is loaded again into
       // a buffer nobody reads any more, which keeps the issue slots unconditional.
-      const int jk = min(j + 1, nblk - 1);
-      const int jv = min(j, nblk - 1);
+      const int jk = blk(min(j + 1, nblk - 1));
+      const int jv = blk(min(j, nblk - 1));
       valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
         dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
       barrier_nofence();  // the DMA stays in flight through the next phase
@@ -510,9 +529,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // Step 0 has no softmax yet: only the loads of K_1 and V_0, then QK^T of
       // block 0 (peeled, so that every vector phase in the loop has work).
       {
-        const int jk = min(1, nblk - 1);
+        const int jk = blk(min(1, nblk - 1));
 #pragma unroll
-        for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, 0, kb1, vb0);
+        for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, blk(0), kb1, vb0);
         barrier_nofence();
         mfma_phase(0, kb0, vb1);
         wait_vmem();
