@@ -142,13 +142,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int G = H_q / H_kv;
 
   // ---- schedule: workgroup -> (batch, head, query tile or pair of tiles)
-  // Causal tiles differ in cost. Paired, every workgroup costs the same and
-  // a head's pairs are dealt one after the other; unpaired (packed sequences)
-  // they are dealt rank by rank over groups of four heads, so that
-  // consecutive workgroups still cost about the same.
+  // Causal tiles differ in cost. Paired, every workgroup costs the same, and
+  // a pair rank is dealt over the G query heads of one key/value head, so
+  // that the workgroups running side by side read the same K/V blocks at the
+  // same steps (with G = 1, a head's pairs one after the other). Unpaired
+  // (packed sequences), tiles are dealt rank by rank over groups of four
+  // heads, so that consecutive workgroups still cost about the same.
   const int n_units = paired ? (n_qtiles + 1) / 2 : n_qtiles;
   const TileAssign ta = assign_tile(blockIdx.x, n_units, G, xcd_remap, (int)(gridDim.x / n_units), false,
-                                    (CAUSAL && !paired) ? 4 : 1);
+                                    (CAUSAL && !paired) ? 4 : (paired ? G : 1));
   const int kvidx = ta.kvidx, gq = ta.gq, tile_rank = ta.tile_rank;
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
