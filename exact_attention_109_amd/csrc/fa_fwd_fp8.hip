@@ -19,13 +19,18 @@
 //    scalar factor c_j = qd * kd_j * scale * log2(e) (one Q block per wave,
 //    one K block per 64-key block) is applied inside the exponent's FMA.
 //  * P is rounded to e4m3 for the PV product. The V block scale rides on P:
-//    x = p * cv_j with cv_j = 64 * vd_j / vd_max, folded into the exponent as
+//    x = p * cv_j with cv_j = 8 * vd_j / vd_max, folded into the exponent as
 //    + log2(cv_j), so that the raw V codes feed the MFMA and the whole output
-//    is multiplied by vd_max / 64 once at the end. The row sums l use the
+//    is multiplied by vd_max / 8 once at the end. The row sums l use the
 //    float32 x before rounding (divided by cv_j per block), so the LSE is as
 //    accurate as the bf16 path's; only the numerator sees the rounding of P.
-//  * The rescale is skipped while the max grows by at most 2^2, so x <= 256
-//    stays inside the e4m3 range (448). Error of one output element:
+//  * The block max is formed only when needed (as in the bf16 forward): a
+//    block whose lane sums of x stay within 2^8 keeps the running max, since
+//    then every x <= 256 is inside the e4m3 range (448). With cv_j <= 8 the 32
+//    values of a lane sum to at most 2^8 against an exact max, so only a max
+//    that rose makes a block take its exponentials twice. The running max
+//    never exceeds the row's final max, so x is never smaller than against the
+//    exact max. Error of one output element:
 //    |dO| <= 2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |v_j| with w the exact
 //    probabilities and L the sum of exp(s - max) (rounding to nearest of x
 //    costs at most 2^-4 * x for normal x and 2^-10 below 2^-6).
@@ -54,8 +59,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kQuantRows = 128;         // rows per scale block
-constexpr float kRescaleSlack = 2.0f;   // log2 units: x <= 2^2 * cv <= 256
-constexpr float kCvMax = 64.0f;         // cv_j = 64 * vd_j / vd_max
+constexpr float kRescaleSlack = 2.0f;   // log2 units: x <= 2^2 * cv <= 32 after a rescale
+constexpr float kCvMax = 8.0f;          // cv_j = 8 * vd_j / vd_max: 32 x values of an exact max sum to <= 2^8
 constexpr float kCvMin = 9.5367431640625e-07f;  // 2^-20: zero V blocks keep l finite
 
 constexpr int kSgValu = 0x402;
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float vmax = 0.f;
   for (int i = lane; i < nbk; i += 64) vmax = fmaxf(vmax, vd[i]);
   vmax = wave_max(vmax);
-  // (floor 2^-100: keeps 64 / vmax finite when every V block is zero)
+  // (floor 2^-100: keeps kCvMax / vmax finite when every V block is zero)
   const float vmax_safe = fmaxf(vmax, 7.88860905e-31f);
   const float inv_vmax = kCvMax / vmax_safe;
 
@@ -321,12 +326,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Vector phase of block j: mask, block max, (rare) rescale, exponentials
-  // with the V scale folded in, float32 row sums, e4m3 packing.
+  // Vector phase of block j: mask, block max and rescale when needed,
+  // exponentials with the V scale folded in, float32 row sums, e4m3 packing.
+  // The block max is formed first only after a block that moved the running
+  // max (and for the first block). Otherwise the exponentials run against the
+  // running max: a lane's sum of x = p * cv within 2^8 bounds every x by 2^8,
+  // inside the e4m3 range (448), and the block stands. A larger sum (a max
+  // that rose) forms the block max, rescales, and takes the block again.
   constexpr int kGroups = NSUB * 4;                // groups of 4 scores per lane
   constexpr int kDmaSlots = 2 * C::DMA_PER_WAVE;
   constexpr int kGroupsPerSlot = kGroups / kDmaSlots;
   static_assert(kGroupsPerSlot * kDmaSlots == kGroups, "DMA slots per exponential group");
+  auto no_dma = [](int) __attribute__((always_inline)) {};
+  bool eager = true;
   auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
     constexpr bool kDma = decltype(has_dma)::value;
     if constexpr (!kDma) {
@@ -335,6 +347,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kblk = (j * BC) / kQuantRows;
     const float c = fmaxf(qd * kd[kblk] * scale_log2, 1.17549435e-38f);
     const float cv = fmaxf(vd[kblk] * inv_vmax, kCvMin);
+    const float lcv = __log2f(cv);
     if (need_mask(j)) {
       const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
       const int lim = last_key - j * BC - 16 * half;
@@ -344,14 +357,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 16; ++i)
           if (32 * n + i > lim) sacc[n][i] = -INFINITY;
     }
-    float mx = sacc[0][0];
+    auto block_max = [&]() __attribute__((always_inline)) {
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int n = 0; n < NSUB; ++n)
+      for (int n = 0; n < NSUB; ++n)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
-    const float m_blk = max_xor32(mx) * c;
-    if (__any(m_blk > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, m_blk);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[n][i]);
+      return max_xor32(mx) * c;
+    };
+    auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -359,38 +373,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[s][i] *= alpha;
       m_run = m_new;
-    }
-    const float bias = __log2f(cv) - m_run;
+    };
     float psum = 0.f;
+    auto exps = [&](auto&& iss, auto dma_here) __attribute__((always_inline)) {
+      constexpr bool kD = decltype(dma_here)::value;
+      const float bias = lcv - m_run;
+      psum = 0.f;
 #pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      const int n = gi >> 2;
-      const int v4 = gi & 3;
-      float x[4];
+      for (int gi = 0; gi < kGroups; ++gi) {
+        const int n = gi >> 2;
+        const int v4 = gi & 3;
+        float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = fast_exp2(fmaf(sacc[n][4 * v4 + e], c, bias));
-        psum += x[e];
+        for (int e = 0; e < 4; ++e) {
+          x[e] = fast_exp2(fmaf(sacc[n][4 * v4 + e], c, bias));
+          psum += x[e];
+        }
+        pk[n >> 1][4 * (n & 1) + v4] = cvt_fp8x4(x[0], x[1], x[2], x[3]);
+        if constexpr (kD) {
+          if ((gi % kGroupsPerSlot) == kGroupsPerSlot - 1) iss(gi / kGroupsPerSlot);
+        }
       }
-      pk[n >> 1][4 * (n & 1) + v4] = cvt_fp8x4(x[0], x[1], x[2], x[3]);
-      if constexpr (kDma) {
-        if ((gi % kGroupsPerSlot) == kGroupsPerSlot - 1) issue(gi / kGroupsPerSlot);
+      if constexpr (kD) {
+#pragma unroll
+        for (int i = 0; i < kDmaSlots; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgValu, 14 * kGroupsPerSlot, 0);
+          __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        }
+      }
+    };
+    bool moved = false;
+    if (eager) {
+      const float m_blk = block_max();
+      if (__any(m_blk > m_run + kRescaleSlack)) {
+        rescale_to(fmaxf(m_run, m_blk));
+        moved = true;
       }
     }
-    if constexpr (kDma) {
-#pragma unroll
-      for (int i = 0; i < kDmaSlots; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgValu, 14 * kGroupsPerSlot, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+    exps(issue, has_dma);
+    if (__any(!(psum <= 256.0f))) {
+      const float m_new = fmaxf(m_run, block_max());
+      // (a sum above 2^8 implies some row's max rose; only NaN inputs can
+      // leave every max unchanged, and then the block stands as computed)
+      if (__any(m_new > m_run)) {
+        rescale_to(m_new);
+        exps(no_dma, std::false_type{});
+        moved = true;
       }
     }
+    eager = moved;
     l_run += psum * __builtin_amdgcn_rcpf(cv);  // v_rcp_f32: 1 ulp
     // keep the row sum in this phase: left alone, the compiler sinks the
     // 32 dependent adds past the phase barrier into the next MFMA phase
     asm volatile("" : "+v"(l_run));
   };
 
-  auto no_dma = [](int) __attribute__((always_inline)) {};
   auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
     mfma_phase(j, k_cur, v_prev);
     barrier_nofence();

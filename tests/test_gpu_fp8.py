@@ -154,7 +154,7 @@ def fp8_bound(c, b, h, G, causal, scale, rows):
     assert np.all(np.isfinite(E))
     r = np.expm1(delta + E[:, None])                                   # relative change of each w_ij
     vdb = np.repeat(c["vd"][b, hk].astype(np.float64), 128)[:k.shape[0]]
-    cv = np.maximum(64.0 * vdb / max(float(c["vd"][b, hk].max()), 1e-38), 2.0 ** -20)
+    cv = np.maximum(8.0 * vdb / max(float(c["vd"][b, hk].max()), 1e-38), 2.0 ** -20)
     wmax = W.max(axis=1, keepdims=True)                               # = 1 / L
     rmax = np.expm1(delta.max(axis=1, keepdims=True) + E[:, None])
     eff = np.maximum(W * (1.0 + r), 2.0 ** -6 * wmax * (1.0 + rmax) / cv[None, :])
