@@ -35,16 +35,17 @@
 //    4-7 (group B) run the same per-block sequence -- an MFMA phase
 //    (PV of block j-1, then QK^T of block j) and a vector phase (mask, max,
 //    exponentials, row sums, bf16 packing of block j) -- with B one phase
-//    behind A, and a workgroup barrier at every phase boundary. At any time
-//    one wave of each SIMD drives the matrix core while its partner runs the
-//    softmax on the vector ALU.
+//    behind A, and one workgroup barrier per block. A block starts with A's
+//    MFMA phase beside B's vector phase; the MFMA phases run at wave priority
+//    2 and B's vector phase at 1, so that the wave that finishes first goes
+//    on to its next phase on the issue slots its partner leaves.
 //  * K and V blocks stream from HBM straight into LDS with 16-byte
 //    global_load_lds_dwordx4 (no register staging, double-buffered), issued
 //    by group B one at a time between the exponentials of its vector phase:
 //    a wave stalls at a vector-memory instruction until the CU's load path
-//    accepts it, so a burst would cost the whole transfer time. The phase
-//    barriers carry no memory fence, so the loads stay in flight across the
-//    next phase and are waited for only before the barrier that publishes them. Tiles are row-major with
+//    accepts it, so a burst would cost the whole transfer time. The block
+//    barriers carry no memory fence, so the loads stay in flight through B's
+//    MFMA phase and are waited for only before the barrier that publishes them. Tiles are row-major with
 //    XOR-swizzled 16-byte chunks chosen so that every LDS read is free of bank
 //    conflicts. The V^T operand is read with ds_read_b64_tr_b16, which
 //    transposes 16-bit elements across lanes.
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     // ---- key blocks visited by the workgroup. Every wave computes all of them:
-    // the phase barriers make a block cost the same time whether or not a wave
+    // the block barriers make a block cost the same time whether or not a wave
     // skips it, and a block entirely past a wave's rows is masked to exact
     // zeros (every row sees key 0 in block 0, so its running max is finite
     // from then on and exp2 of a masked score is 0).
@@ -370,6 +371,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
       const bool do_pv = j >= 1;
       const bool do_qk = j < nblk;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
+      __builtin_amdgcn_sched_barrier(0);
       if (do_pv) {
         pv_part(vt);
         pv_schedule();
@@ -380,6 +384,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         qk_schedule();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     // Vector phase for block j: mask, block max, (rare) rescale, exponentials,
@@ -484,19 +491,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       l_run += psum;
     };
 
-    // Two phases (ticks) per block j. Group A: MFMA(j) | VALU(j).
-    // Group B: VALU(j-1) + DMA of K_{j+1}, V_j | MFMA(j), then wait for the DMA.
-    // The phase barriers carry no memory fence: every LDS read of a phase is
-    // consumed by an MFMA of the same phase, so a buffer is free for the next
-    // DMA once the barrier after its last reading phase has passed, and DMA
-    // data is waited for explicitly one phase after it was issued.
+    // One barrier per block j. Group A: MFMA(j), VALU(j). Group B: VALU(j-1)
+    // + DMA of K_{j+1}, V_j, MFMA(j), then wait for the DMA. The DMA of block
+    // j overwrites the buffers of K_{j-1} and V_{j-2}, which both groups last
+    // read in their MFMA phases of block j-1, before the barrier that starts
+    // block j. The barriers carry no memory fence: every LDS read of a phase
+    // is consumed by an MFMA of the same phase, and DMA data is waited for
+    // explicitly before the barrier that publishes it. Wave priorities (MFMA
+    // phases 2, B's vector phase 1, A's 0) keep the block's order: A's MFMA
+    // beside B's softmax, then B's MFMA beside A's softmax, with the wave that
+    // finishes early running ahead on the issue slots the other leaves.
     // Buffers: step j's K and V blocks in kb[j%2], vb[j%2]. Each group runs its own loop
     // (the group test is outside the loop, so the compiler never has to keep
     // both groups' register state alive across the barriers); both loops pass
-    // the same 2*(nblk+1) barriers.
+    // the same nblk+1 barriers.
     auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
       mfma_phase(j, k_cur, v_prev);
-      barrier_nofence();
       valu_phase(j, no_dma, std::false_type{});
       barrier_nofence();
     };
@@ -506,9 +516,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // a buffer nobody reads any more, which keeps the issue slots unconditional.
       const int jk = blk(min(j + 1, nblk - 1));
       const int jv = blk(min(j, nblk - 1));
+      // B's vector phase, which the block waits for, takes issue precedence
+      // over A's, which starts as soon as A's MFMA phase ends
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
       valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
         dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
-      barrier_nofence();  // the DMA stays in flight through the next phase
       mfma_phase(j, k_cur, v_prev);
       wait_vmem();        // K_{j+1} and V_j are in LDS before the barrier publishes them
       barrier_nofence();
@@ -534,7 +548,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int jk = blk(min(1, nblk - 1));
 #pragma unroll
         for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, blk(0), kb1, vb0);
-        barrier_nofence();
         mfma_phase(0, kb0, vb1);
         wait_vmem();
         barrier_nofence();

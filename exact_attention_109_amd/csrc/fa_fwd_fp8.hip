@@ -37,7 +37,8 @@
 //
 // gfx950 mapping: as the bf16 forward (8 waves in two ping-pong groups of 4,
 // 256 query rows per workgroup, LDS-DMA double buffering issued between the
-// exponentials of group B, fence-free phase barriers), with:
+// exponentials of group B, one fence-free barrier per block, MFMA phases at
+// wave priority 2 and group B's vector phase at 1), with:
 //  * the FP8 MFMA operand: lane l holds row l%32 and k = 32*(l/32) + byte;
 //    S^T tile n (keys 32n .. 32n+31, A-row permutation row_of_lane) leaves
 //    keys 32n + 16g + i in register i of lane half g, so the 32 P bytes of a
@@ -292,9 +293,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
   // The MFMA phase runs at raised wave priority, so that its LDS reads and
-  // MFMAs win issue arbitration against the vector phase of the partner wave
-  // on the same SIMD (the vector phase is the longer one; the matrix core
-  // should not wait for it).
+  // MFMAs win issue arbitration against the vector phases on the same SIMD
+  // (the vector phase is the longer one; the matrix core should not wait for
+  // it).
   auto mfma_phase = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     const bool do_pv = j >= 1;
     const bool do_qk = j < nblk;
@@ -424,13 +425,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     eager = moved;
     l_run += psum * __builtin_amdgcn_rcpf(cv);  // v_rcp_f32: 1 ulp
     // keep the row sum in this phase: left alone, the compiler sinks the
-    // 32 dependent adds past the phase barrier into the next MFMA phase
+    // 32 dependent adds past the end of the phase into the next MFMA phase
     asm volatile("" : "+v"(l_run));
   };
 
   auto block_a = [&](int j, const uint8_t* k_cur, const uint8_t* v_prev) __attribute__((always_inline)) {
     mfma_phase(j, k_cur, v_prev);
-    barrier_nofence();
     valu_phase(j, no_dma, std::false_type{});
     barrier_nofence();
   };
@@ -438,9 +438,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       __attribute__((always_inline)) {
     const int jk = min(j + 1, nblk - 1);
     const int jv = min(j, nblk - 1);
+    // B's vector phase, which the block waits for, takes issue precedence
+    // over A's, which starts as soon as A's MFMA phase ends
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     valu_phase(j - 1, [&](int i) __attribute__((always_inline)) {
       dma_slot(i, jk, jv, k_dma, v_dma); }, std::true_type{});
-    barrier_nofence();
     mfma_phase(j, k_cur, v_prev);
     wait_vmem();
     barrier_nofence();
@@ -462,7 +466,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int jk = min(1, nblk - 1);
 #pragma unroll
       for (int i = 0; i < kDmaSlots; ++i) dma_slot(i, jk, 0, kb1, vb0);
-      barrier_nofence();
       mfma_phase(0, kb0, vb1);
       wait_vmem();
       barrier_nofence();
