@@ -12,19 +12,16 @@
 // --------------
 //  * Workgroup = 8 wave64s, 256 query rows (32 per wave), one workgroup per
 //    CU (2 waves per SIMD). All tiles of one key/value head go to one XCD.
-//    Causal dense calls at d = 128: a workgroup takes two tiles of one head,
-//    r and n-1-r, one after the other, so that every workgroup costs the same
+//    Causal calls at d = 128 (dense, or packed with n counted per sequence):
+//    a workgroup takes two tiles of one head, r and n-1-r, one after the
+//    other, so that every workgroup of a head costs the same
 //    (the dispatcher starts an XCD's workgroups a few at a time and in order,
 //    so unequal neighbours leave compute units idle) while one head's tiles
 //    stay neighbours in the grid (their K/V is shared through L2). The
 //    lighter tile runs second and visits its key blocks from the diagonal
 //    down, so that all workgroups of a head read the same K/V block at each
-//    step of both tiles. Otherwise
-//    one workgroup per (batch, query head, 256-row tile), causal tiles
-//    heaviest first and dealt rank by rank over groups of four heads. (At
-//    d = 64 the loop over two tiles would keep values from outside the block
-//    loop alive through it and push the kernel past 256 registers into
-//    spills inside the loop.)
+//    step of both tiles. Non-causal calls take one workgroup per (batch,
+//    query head, 256-row tile). (d = 64 runs the rotation kernel below.)
 //  * Contractions on v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The
 //    scores are computed transposed, S^T = K Q^T (K as the A operand, Q as B),
 //    so that a lane owns one query column; P^T then feeds O^T = V^T P^T as the
@@ -146,9 +143,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Causal tiles differ in cost. Paired, every workgroup costs the same, and
   // a pair rank is dealt over the G query heads of one key/value head, so
   // that the workgroups running side by side read the same K/V blocks at the
-  // same steps (with G = 1, a head's pairs one after the other). Unpaired
-  // (packed sequences), tiles are dealt rank by rank over groups of four
-  // heads, so that consecutive workgroups still cost about the same.
+  // same steps (with G = 1, a head's pairs one after the other). Packed
+  // sequences pair the tiles of each sequence by its own tile count; pair
+  // ranks past a short sequence end at once. Unpaired (d = 64), causal tiles
+  // are dealt rank by rank over groups of four heads, so that consecutive
+  // workgroups still cost about the same.
   const int n_units = paired ? (n_qtiles + 1) / 2 : n_qtiles;
   const TileAssign ta = assign_tile(blockIdx.x, n_units, G, xcd_remap, (int)(gridDim.x / n_units), false,
                                     (CAUSAL && !paired) ? 4 : (paired ? G : 1));
@@ -156,8 +155,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int b = kvidx / H_kv;
   const int hk = kvidx % H_kv;
   const int h = hk * G + gq;
-  const int tile_hi = CAUSAL ? (n_qtiles - 1 - tile_rank) : tile_rank;  // heaviest first
-  const int n_it = (D == 128 && paired && tile_rank != tile_hi) ? 2 : 1;  // (launch sets paired only at d = 128)
 
   // Dense: q, o [B][H_q][N_q][D], k, v [B][H_kv][N_kv][D], lse [B][H_q][N_q].
   // Packed sequences (cu_q != null): b is a sequence, q, o [H_q][total_q][D],
@@ -183,7 +180,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kvbase = (size_t(b) * H_kv + hk) * size_t(N_kv) * D;
     lbase = (size_t(b) * H_q + h) * size_t(N_q);
   }
-  // tiles of this workgroup: the heavier one first, then (paired) its mirror
+  // tiles of this workgroup: the heavier one first, then (paired) its mirror,
+  // counted in the sequence's own tiles
+  const int n_seq = paired ? (N_q + kBR - 1) / kBR : n_qtiles;
+  if (paired && tile_rank >= (n_seq + 1) / 2) return;  // (whole workgroup) past a short sequence
+  const int tile_hi = CAUSAL ? (n_seq - 1 - tile_rank) : tile_rank;  // heaviest first
+  const int n_it = (D == 128 && paired && tile_rank != tile_hi) ? 2 : 1;  // (launch sets paired only at d = 128)
   for (int it = 0; it < n_it; ++it) {
     const int tile = it == 0 ? tile_hi : tile_rank;
     const int q0 = tile * kBR;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int j = 0; j < D / 2; j += 4) st_global8(op + j, u32x2{0u, 0u});
         if (half == 0) LSE[lbase + row] = -INFINITY;
       }
-      return;
+      continue;
     }
     const uint8_t* __restrict__ Kbytes = reinterpret_cast<const uint8_t*>(K + kvbase);
     const uint8_t* __restrict__ Vbytes = reinterpret_cast<const uint8_t*>(V + kvbase);
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, const VarlenParams* vl, hipStream_t stream) {
   const int n_qtiles = (p.N_q + kBR - 1) / kBR;
-  const int paired = (D == 128 && CAUSAL && vl == nullptr) ? 1 : 0;
+  const int paired = (D == 128 && CAUSAL) ? 1 : 0;
   const long long nwg = (long long)(paired ? (n_qtiles + 1) / 2 : n_qtiles) * p.B * p.H_q;
   const int xcd_remap = ((p.B * p.H_kv) % 8 == 0) ? 1 : 0;
   // Masked scores are -inf and exp2(-inf * c) must be 0, so c stays positive:

@@ -41,6 +41,8 @@ CASES = [
     ([3, 10], [0, 10], 2, 1, 128, False),                        # a sequence without keys
     ([3, 10, 6], [0, 10, 70], 2, 1, 64, True),                   # the same at d = 64, causal
     ([600, 5], [600, 700], 2, 2, 64, True),                      # d = 64, two 512-row query tiles
+    ([300, 600, 10], [300, 0, 10], 2, 1, 128, True),            # causal tile pairs; no keys over three tiles
+    ([0, 700, 5], [9, 700, 5], 2, 2, 128, True),                 # causal tile pairs; a sequence without queries
 ]
 
 
