@@ -340,15 +340,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   static_assert(kGroupsPerSlot * kDmaSlots == kGroups, "DMA slots per exponential group");
   auto no_dma = [](int) __attribute__((always_inline)) {};
   bool eager = true;
+  // factors of the current 128-key scale block (two key blocks share one)
+  int f_kblk = -1;
+  float f_c = 0.f, f_cv = 1.f, f_lcv = 0.f, f_rcv = 1.f;
   auto valu_phase = [&](int j, auto&& issue, auto has_dma) __attribute__((always_inline)) {
     constexpr bool kDma = decltype(has_dma)::value;
     if constexpr (!kDma) {
       if (j >= nblk) return;
     }
     const int kblk = (j * BC) / kQuantRows;
-    const float c = fmaxf(qd * kd[kblk] * scale_log2, 1.17549435e-38f);
-    const float cv = fmaxf(vd[kblk] * inv_vmax, kCvMin);
-    const float lcv = __log2f(cv);
+    if (kblk != f_kblk) {
+      f_kblk = kblk;
+      f_c = fmaxf(qd * kd[kblk] * scale_log2, 1.17549435e-38f);
+      f_cv = fmaxf(vd[kblk] * inv_vmax, kCvMin);
+      f_lcv = __log2f(f_cv);
+      f_rcv = __builtin_amdgcn_rcpf(f_cv);  // v_rcp_f32: 1 ulp
+    }
+    const float c = f_c;
+    const float lcv = f_lcv;
     if (need_mask(j)) {
       const int last_key = CAUSAL ? min(qrow, N_kv - 1) : N_kv - 1;
       const int lim = last_key - j * BC - 16 * half;
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     eager = moved;
-    l_run += psum * __builtin_amdgcn_rcpf(cv);  // v_rcp_f32: 1 ulp
+    l_run += psum * f_rcv;
     // keep the row sum in this phase: left alone, the compiler sinks the
     // 32 dependent adds past the end of the phase into the next MFMA phase
     asm volatile("" : "+v"(l_run));
