@@ -187,12 +187,9 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ __attribute__((aligned(1024))) u32x4 pex[4][C::STEPS][64];   // [pair][packed P register][lane], bf16
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pw = wave & 3;         // pair index = 32-key sub-tile = SIMD
   const bool is_ds = wave >= 4;    // wave-uniform role
-  const int col = lane & 31;
-  const int half = lane >> 5;
   const int G = H_q / H_kv;
 
   // Causal: a workgroup takes key tiles r and n-1-r of one head (tile r has

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(const void* __rest
   }
   part[threadIdx.x] = acc;
   __syncthreads();
-  for (int w = kCheckThreads / 2; w > 0; w >>= 1) {
+  for (unsigned w = kCheckThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
     __syncthreads();
   }
