@@ -389,10 +389,11 @@ def _mutant_forward(kind):
                 allowed = keys >= rows[:, None]
             S = np.where(allowed, S, -np.inf)
         m = S.max(axis=1, keepdims=True)
-        P = np.exp(S - m)
-        l = P.sum(axis=1, keepdims=True)
-        if kind != "no_normalize":
-            P = P / l
+        with np.errstate(invalid="ignore", divide="ignore"):  # a strict mask leaves row 0 without keys
+            P = np.exp(S - m)
+            l = P.sum(axis=1, keepdims=True)
+            if kind != "no_normalize":
+                P = P / l
         out = P @ v
         if kind == "lse_log2":
             lse = (m + np.log2(l))[:, 0]
