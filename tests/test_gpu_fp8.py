@@ -208,6 +208,20 @@ def test_fwd_fp8_zero_v_block_and_wide_spread():
     print(f"largest error as a fraction of its bound: {worst:.3f}")
 
 
+def test_fwd_fp8_score_jumps_take_the_block_again():
+    """K block scales that jump by 4x every three scale blocks (384 keys; no
+    other spread): a jump lands on a key block whose predecessor left the
+    running max alone, so the kernel takes its exponentials against the stale
+    max, finds a lane sum above 2^8, forms the block max and takes the block
+    again. Every element stays within its bound, causal and not."""
+    c = make_fp8_case(1, 2, 2, 900, 900, 128, seed=81, spread=(0, 0))
+    for i in range(c["kd"].shape[2]):
+        c["kd"][:, :, i] = c["kd"][:, :, i] * np.float32(4.0 ** (i // 3))
+    for causal in (False, True):
+        worst = check_case(c, 1, 2, 2, 900, causal, default_scale(128))
+        print(f"causal={causal}: largest error as a fraction of its bound: {worst:.3f}")
+
+
 def test_fwd_fp8_uniform_attention_is_exact():
     """q = 0: every allowed key has weight 1/count; with power-of-two V block
     scale ratios every rounded probability is exact, so O is the mean of V up
