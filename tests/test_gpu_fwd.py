@@ -143,6 +143,30 @@ def test_config_parity(name):
     assert el <= tol["lse"], el
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_logits_d64(causal):
+    """Q and K x 8 at d = 64 (the rotation kernel): nearly one-hot rows whose
+    running max moves in many blocks, so the block max is formed and blocks
+    are taken again often. Every element against the oracle, under the
+    extreme-logit bound of c4x."""
+    import torch
+    import exact_attention_109_amd as fa
+    B, H_q, H_kv, N, d = 1, 4, 2, 1100, 64
+    inp = make_inputs_shape(DTYPE_BF16, B, H_q, H_kv, N, N, d, seed=433 + causal, qk_multiplier=8.0)
+    scale = default_scale(d)
+    q, k, v = upload(inp)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    O, L = oracle_forward_all(inp.f64("q"), inp.f64("k"), inp.f64("v"), causal, scale, H_q // H_kv)
+    n_past = o_extreme_check(o, O, inp.f64("q"), inp.f64("k"), inp.f64("v"), causal, scale, H_q // H_kv)
+    el = max_abs(lse, L)
+    print(f"causal={causal}: max-abs O {max_abs(o, O):.3e} ({n_past} past 1e-2 + half an ulp), LSE {el:.3e}, "
+          f"max|O| {np.abs(O).max():.2f}")
+    assert el <= TOL[DTYPE_BF16]["lse"], el
+
+
 def test_q_zero_closed_form_full_size():
     """Q = 0 makes every row uniform over its allowed keys (c3 shape)."""
     import torch
