@@ -277,11 +277,11 @@ int fa_quantize_fp8(const void* x, void* codes, float* descale, int B, int H, in
  * matrix instructions ("深度学习进阶（三十一）FlashAttention：IO 感知的精确注意力"
  * (rkmt.cn blog), version comparison table: FP8 is one of FlashAttention-3's
  * additions). The scores and the row sums are float32; the probabilities
- * are rounded to e4m3 (after multiplication by 64 * vd / vd_max of their V
+ * are rounded to e4m3 (after multiplication by 8 * vd / vd_max of their V
  * block) for the P V product only, so one output element is within
  *     2^-4 * sum_j max(w_j, 2^-6 / (cv_j * L)) * |V_j|
  * of the exact value (w the exact probabilities, L = sum_j exp(s_j - max s),
- * cv_j = 64 * vd_j / vd_max), plus float32 and bf16 output rounding; the
+ * cv_j = 8 * vd_j / vd_max), plus float32 and bf16 output rounding; the
  * LSE is as accurate as fa_fwd's in bf16.
  *   q8 [B][H_q][N_q][d], k8 and v8 [B][H_kv][N_kv][d]: row-major codes
  *       (fa_quantize_fp8 with d_major = 0);
