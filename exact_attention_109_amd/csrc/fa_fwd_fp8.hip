@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- epilogue: O = O_acc * (vd_max / 64) / l, LSE = ln2 * (m + log2 l)
+  // ---- epilogue: O = O_acc * (vd_max / kCvMax) / l, LSE = ln2 * (m + log2 l)
   const float l_tot = sum_xor32(l_run);
   if (qrow < N_q) {
     const float f = (vmax_safe / kCvMax) / l_tot;
