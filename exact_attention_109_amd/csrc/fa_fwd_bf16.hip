@@ -42,9 +42,9 @@
 //    a wave stalls at a vector-memory instruction until the CU's load path
 //    accepts it, so a burst would cost the whole transfer time. The block
 //    barriers carry no memory fence, so the loads stay in flight through B's
-//    MFMA phase and are waited for only before the barrier that publishes them. Tiles are row-major with
-//    XOR-swizzled 16-byte chunks chosen so that every LDS read is free of bank
-//    conflicts. The V^T operand is read with ds_read_b64_tr_b16, which
+//    MFMA phase and are waited for only before the barrier that publishes
+//    them. Tiles are row-major with XOR-swizzled 16-byte chunks chosen so
+//    that every LDS read is free of bank conflicts. The V^T operand is read with ds_read_b64_tr_b16, which
 //    transposes 16-bit elements across lanes.
 //  * Softmax in base 2: scores are multiplied by scale*log2(e) inside one FMA
 //    and exponentiated with v_exp_f32; LSE is converted back with ln 2. The
@@ -53,8 +53,9 @@
 //    running max first and the block max is formed only if some row's block
 //    sum exceeds 2^8 (then the max is raised, O and l rescaled, and the
 //    exponentials taken again); after a block that moved the max, the next
-//    one forms its max first. On the vector ALU, which bounds the loop, this
-//    saves the max of every other block.
+//    one forms its max first. This takes the max off most blocks' vector
+//    phase, one of the loop's two bounds (the other is the MFMA phase's
+//    operand reads from LDS).
 //  * Causal: K/V blocks past the tile's last row are never loaded; masking
 //    runs only on blocks that cross a wave's diagonal or the end of the keys.
 //  * d = 64 runs fwd_bf16_rot_kernel (below): four waves per SIMD in a
