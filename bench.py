@@ -517,8 +517,9 @@ def main():
     _NO_CLOCK_SAMPLE = args.no_clock_sample
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path is "
-              "single-GPU; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the attention path runs on "
+              "one GPU (across GPUs it would shard over (batch, key/value head) pairs with no communication, "
+              "each GPU running the same kernels on its share).", file=sys.stderr)
         sys.exit(2)
 
     import torch
