@@ -19,14 +19,13 @@
 //          exponentials run beside the other's MFMAs. The query blocks of
 //          every query head of the group stream past through LDS (dO and Q
 //          read transposed with ds_read_b64_tr_b16 for dV and dK).
-//  * dq:   one workgroup per (batch, query head, 128-query tile); each wave
-//          owns 32 queries (Q and dO as register operands) while the K/V
-//          blocks stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, then
-//          dQ^T += K^T dS^T with K read transposed. Two workgroups share a
-//          compute unit (240 registers per wave, 64 KiB of LDS each), so the
-//          MFMAs of one wave run beside the vector work of the other wave on
-//          its SIMD; K/V of block j+1 arrive by LDS-DMA while block j is
-//          processed.
+//  * dq:   one workgroup of 8 waves per (batch, query head, 256-query tile);
+//          each wave owns 32 queries (Q and dO as register operands) while
+//          the K/V blocks stream through a 3-deep LDS ring by LDS-DMA:
+//          S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T with K
+//          read transposed. Two groups of four waves run in opposite phases
+//          (one barrier at each phase boundary), so one group's MFMAs run
+//          beside the other group's vector work on every SIMD.
 // The accumulator layouts are arranged so that P and dS leave the MFMA
 // accumulators already in the k-layout of the next contraction's B operand
 // (see row_of_lane), and every LDS tile uses one XOR swizzle that is free of
